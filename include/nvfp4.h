@@ -1,0 +1,169 @@
+/*
+ * nvfp4.h - C ABI of the NVFP4 W4A4 linear layer for AMD MI355X (gfx950).
+ *
+ * The layer (sources: "Why Gated DeltaNet Survives 4-Bit Quantization: NVFP4 W4A4
+ * for the Recurrent Half of a Hybrid 27B LLM", review page):
+ *   - NVFP4 tensor = 4-bit E2M1 values + one E4M3 scale per 16-element block +
+ *     one FP32 global scale per tensor (background section, the paper's section 1;
+ *     Key Numbers list).
+ *   - the block maximum sets the block scale (mechanism step 1, the paper's
+ *     sections 2 and 5.1).
+ *   - modules calibrated separately but served as one fused GEMM keep one global
+ *     scale per module; the GEMM epilogue applies each segment's own scale
+ *     (strengths paragraph, the paper's section 6; the paper's abstract).
+ *   - GDN gates g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b)
+ *     (mechanism step 2, Eq. 1).
+ *
+ * Numerics (identical for every entry point and every kernel variant):
+ *   global scale (dynamic mode)  g = fp32(amax / 2688), 2688 = 6 * 448
+ *   block scale  s = E4M3(t), t = amax_block / (6 g) exactly, round-to-nearest-even,
+ *                saturated at 448; byte 0x00 for a zero block, g == 0 or t <= 2^-10
+ *   element code RNE of |x| / (s g) (exact quotient) onto {0,.5,1,1.5,2,3,4,6},
+ *                saturated at 6, ties to the even code; bit 3 = sign bit of x
+ *   packing      codes [rows][K/2] bytes, low nibble = even element;
+ *                scales [rows][K/16] E4M3 (OCP FN) bytes, row-major, unswizzled
+ *   GEMM         y[m,n] = sum_k (e2m1*s_a)(e2m1*s_w) accumulated in fp32, times
+ *                g_a * g_w[segment(n)], rounded once to the output dtype (RNE)
+ *
+ * Conventions for every function:
+ *   - Returns NVFP4_OK (0) when the work was enqueued on `stream`, else an error
+ *     code; nvfp4_last_error() then gives a message (thread-local).
+ *   - Arguments are validated on the host before anything is enqueued; nothing
+ *     synchronizes.  No exception, abort or exit crosses the ABI.
+ *   - The caller owns every buffer.  The library allocates and frees no user
+ *     memory and keeps no state between calls.
+ *   - "device" pointers point to memory of the current HIP device; "host"
+ *     pointers are read during the call only.  `stream` is a hipStream_t (NULL =
+ *     the null stream).
+ *   - Inputs containing NaN or Inf are outside the contract (results unspecified).
+ *   - Errors: NVFP4_ERR_INVALID_ARG (null pointer, size <= 0, K % 16 != 0,
+ *     ld < K, bad segment table, gate shape mismatch), NVFP4_ERR_UNSUPPORTED
+ *     (dtype or alignment outside the supported set), NVFP4_ERR_DEVICE (current
+ *     device is not gfx950), NVFP4_ERR_HIP (a HIP launch error).
+ *   - Alignment: x, w, y and the packed buffers must be 16-byte aligned, and
+ *     ldx/ldw/ldy must keep every row 16-byte aligned (NVFP4_ERR_UNSUPPORTED
+ *     otherwise).
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define NVFP4_API __attribute__((visibility("default")))
+#else
+#define NVFP4_API
+#endif
+
+#define NVFP4_ABI_VERSION 1
+#define NVFP4_MAX_SEGMENTS 64
+
+enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARG = 1,
+  NVFP4_ERR_UNSUPPORTED = 2,
+  NVFP4_ERR_HIP = 3,
+  NVFP4_ERR_DEVICE = 4
+};
+
+enum nvfp4_dtype {
+  NVFP4_DTYPE_F32 = 0,
+  NVFP4_DTYPE_BF16 = 1
+};
+
+/* GDN gate epilogue parameters (Eq. 1 of the review page, mechanism step 2).
+ * The GEMM must have N == 2 * n_heads: columns [0, n_heads) are the a-heads,
+ * [n_heads, 2 n_heads) the b-heads.  Output row m = [g_0..g_{H-1} | beta_0..beta_{H-1}],
+ * fp32.  A_log and dt_bias are device arrays of n_heads fp32. */
+typedef struct nvfp4_gate_params {
+  int32_t n_heads;
+  const float* A_log;
+  const float* dt_bias;
+} nvfp4_gate_params;
+
+/* ABI version of the loaded library (NVFP4_ABI_VERSION). */
+NVFP4_API int32_t nvfp4_abi_version(void);
+
+/* Message of the last error on this thread ("" if none).  Valid until the next call. */
+NVFP4_API const char* nvfp4_last_error(void);
+
+/*
+ * Activation quantization (the first stage of the layer).
+ *   x         device, [M rows][ldx elements], dtype x_dtype (F32 or BF16)
+ *   gscale_in device, 1 fp32: calibrated global scale (static mode), or NULL:
+ *             dynamic mode, g = fp32(amax(x) / 2688) computed on the device
+ *             (dynamic-mode scales from the tensor itself: "SoloQ" page,
+ *             usage/assumptions section)
+ *   codes     device, [M][K/2] bytes (output)
+ *   scales    device, [M][K/16] bytes (output)
+ *   gscale_out device, 1 fp32 (output): the global scale used (a copy of
+ *             *gscale_in in static mode).  In dynamic mode it is also the
+ *             reduction target, so it must not alias x.
+ */
+NVFP4_API int32_t nvfp4_quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                           const float* gscale_in, uint8_t* codes, uint8_t* scales,
+                           float* gscale_out, void* stream);
+
+/*
+ * Offline weight packing with one global scale per fused-output segment (module).
+ *   w             device, [N rows][ldw elements], F32 or BF16; row n is output column n
+ *   n_seg, seg_end host, n_seg (1..NVFP4_MAX_SEGMENTS) strictly increasing row ends,
+ *                 seg_end[n_seg-1] == N; segment i covers rows [seg_end[i-1], seg_end[i])
+ *   seg_gscale_in host, n_seg fp32 calibrated scales (finite, >= 0), or NULL:
+ *                 each segment gets fp32(amax(segment) / 2688)
+ *   codes, scales device outputs as for nvfp4_quantize_act ([N][K/2], [N][K/16])
+ *   seg_gscale_out device, n_seg fp32 (output): the scales used
+ */
+NVFP4_API int32_t nvfp4_pack_weight(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
+                          int32_t n_seg, const int64_t* seg_end, const float* seg_gscale_in,
+                          uint8_t* codes, uint8_t* scales, float* seg_gscale_out, void* stream);
+
+/*
+ * Block-scaled W4A4 GEMM with the per-segment global-scale epilogue
+ * (the repair for fused GEMMs over per-module-calibrated weights) and an
+ * optional GDN gate epilogue.
+ *   a_codes, a_scales device, quantized activations [M][K/2], [M][K/16]
+ *   a_gscale          device, 1 fp32
+ *   w_codes, w_scales device, packed weight [N][K/2], [N][K/16]
+ *   n_seg, seg_end    host segment table over N (as for nvfp4_pack_weight)
+ *   w_seg_gscale      device, n_seg fp32
+ *   gate              host struct or NULL; non-NULL requires N == 2 * gate->n_heads
+ *                     and y_dtype == F32
+ *   y                 device, [M][ldy] of y_dtype (F32 or BF16), output
+ */
+NVFP4_API int32_t nvfp4_w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                        int64_t M, int64_t N, int64_t K,
+                        const uint8_t* w_codes, const uint8_t* w_scales,
+                        int32_t n_seg, const int64_t* seg_end, const float* w_seg_gscale,
+                        const nvfp4_gate_params* gate,
+                        void* y, int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
+ * The whole layer in one call: activation quantization + GEMM + epilogues.
+ * Results equal nvfp4_quantize_act followed by nvfp4_w4a4_gemm.  Decode shapes
+ * (M <= 8) and skinny shapes (N <= 128) run fused kernels that quantize x in
+ * registers; other shapes run the two stages and then need a_codes_out and
+ * a_scales_out as the place to put the quantized activations.
+ *   x, x_dtype, M, K, ldx, gscale_in   as for nvfp4_quantize_act
+ *   gscale_out     device, 1 fp32 (output): the activation global scale used
+ *   N, w_*, n_seg, seg_end, w_seg_gscale, gate, y, y_dtype, ldy  as for nvfp4_w4a4_gemm
+ *   a_codes_out, a_scales_out  device [M][K/2], [M][K/16] or NULL.  When given,
+ *                  they receive the activation codes and scales on every path.
+ */
+NVFP4_API int32_t nvfp4_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                          const float* gscale_in, float* gscale_out,
+                          int64_t N, const uint8_t* w_codes, const uint8_t* w_scales,
+                          int32_t n_seg, const int64_t* seg_end, const float* w_seg_gscale,
+                          const nvfp4_gate_params* gate,
+                          void* y, int32_t y_dtype, int64_t ldy,
+                          uint8_t* a_codes_out, uint8_t* a_scales_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

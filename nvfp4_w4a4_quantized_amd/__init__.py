@@ -1,0 +1,178 @@
+"""Python binding of libnvfp4.so, the NVFP4 W4A4 linear layer for MI355X (gfx950).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels behind
+the C ABI declared in include/nvfp4.h.  torch tensors supply device memory and the
+current HIP stream.  The functions carry the C names and raise Nvfp4Error with the
+library's message when a call returns an error status.
+
+Importing this package loads the library and raises ImportError if it has not
+been built (``python -m nvfp4_w4a4_quantized_amd.build``); there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+NVFP4_OK = 0
+NVFP4_ERR_INVALID_ARG = 1
+NVFP4_ERR_UNSUPPORTED = 2
+NVFP4_ERR_HIP = 3
+NVFP4_ERR_DEVICE = 4
+NVFP4_DTYPE_F32 = 0
+NVFP4_DTYPE_BF16 = 1
+NVFP4_MAX_SEGMENTS = 64
+
+EXPORTED = ["nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize_act", "nvfp4_pack_weight",
+            "nvfp4_w4a4_gemm", "nvfp4_w4a4_linear"]
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"nvfp4 status {status}: {msg}")
+        self.status = status
+
+
+class GateParams(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m nvfp4_w4a4_quantized_amd.build` "
+                          "(the NVFP4 layer has no non-HIP implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.nvfp4_abi_version.restype = I32
+    lib.nvfp4_abi_version.argtypes = []
+    lib.nvfp4_last_error.restype = ctypes.c_char_p
+    lib.nvfp4_last_error.argtypes = []
+    lib.nvfp4_quantize_act.restype = I32
+    lib.nvfp4_quantize_act.argtypes = [P, I32, I64, I64, I64, P, P, P, P, P]
+    lib.nvfp4_pack_weight.restype = I32
+    lib.nvfp4_pack_weight.argtypes = [P, I32, I64, I64, I64, I32, P, P, P, P, P, P]
+    lib.nvfp4_w4a4_gemm.restype = I32
+    lib.nvfp4_w4a4_gemm.argtypes = [P, P, P, I64, I64, I64, P, P, I32, P, P, P, P, I32, I64, P]
+    lib.nvfp4_w4a4_linear.restype = I32
+    lib.nvfp4_w4a4_linear.argtypes = [P, I32, I64, I64, I64, P, P, I64, P, P, I32, P, P, P, P, I32, I64, P, P, P]
+    return lib
+
+
+lib = _load()
+
+
+def nvfp4_abi_version() -> int:
+    return int(lib.nvfp4_abi_version())
+
+
+def nvfp4_last_error() -> str:
+    return lib.nvfp4_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != NVFP4_OK:
+        raise Nvfp4Error(status, nvfp4_last_error())
+
+
+# ----------------------------------------------------------------------------- torch glue
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return NVFP4_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return NVFP4_DTYPE_BF16
+    raise Nvfp4Error(NVFP4_ERR_UNSUPPORTED, f"dtype {t.dtype} is not float32 or bfloat16")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _rows(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise Nvfp4Error(NVFP4_ERR_INVALID_ARG, f"{name} must be 2-D with unit column stride")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _seg_array(seg_end: Sequence[int]):
+    arr = (ctypes.c_int64 * len(seg_end))(*[int(v) for v in seg_end])
+    return arr, len(seg_end)
+
+
+def _gate(gate):
+    if gate is None:
+        return None
+    A_log, dt_bias = gate
+    return GateParams(int(A_log.numel()), A_log.data_ptr(), dt_bias.data_ptr())
+
+
+def empty_packed(rows: int, K: int, device="cuda"):
+    """Device buffers (codes [rows, K/2], scales [rows, K/16]) for a packed operand."""
+    torch = _torch()
+    return (torch.empty((rows, K // 2), dtype=torch.uint8, device=device),
+            torch.empty((rows, K // 16), dtype=torch.uint8, device=device))
+
+
+def nvfp4_quantize_act(x, gscale_in, codes, scales, gscale_out, stream=None) -> None:
+    """Quantize activations x [M, K] (bf16/fp32).  gscale_in None = dynamic mode."""
+    M, K, ldx = _rows(x, "x")
+    _check(lib.nvfp4_quantize_act(x.data_ptr(), _dtype_code(x), M, K, ldx, _ptr(gscale_in), codes.data_ptr(),
+                                  scales.data_ptr(), gscale_out.data_ptr(), _stream(stream)))
+
+
+def nvfp4_pack_weight(w, seg_end, seg_gscale_in, codes, scales, seg_gscale_out, stream=None) -> None:
+    """Pack weight w [N, K] with per-segment global scales.  seg_gscale_in: list of
+    host floats (calibrated) or None (per-segment amax)."""
+    N, K, ldw = _rows(w, "w")
+    seg, n_seg = _seg_array(seg_end)
+    gin = None
+    if seg_gscale_in is not None:
+        gin = (ctypes.c_float * n_seg)(*[float(v) for v in seg_gscale_in])
+    _check(lib.nvfp4_pack_weight(w.data_ptr(), _dtype_code(w), N, K, ldw, n_seg, seg, gin, codes.data_ptr(),
+                                 scales.data_ptr(), seg_gscale_out.data_ptr(), _stream(stream)))
+
+
+def nvfp4_w4a4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_end, w_seg_gscale, y, gate=None,
+                    stream=None) -> None:
+    """y = GEMM of packed operands with the per-segment epilogue (and the gate
+    epilogue if gate = (A_log, dt_bias) is given)."""
+    M, half_k = a_codes.shape
+    N = w_codes.shape[0]
+    _, _, ldy = _rows(y, "y")
+    seg, n_seg = _seg_array(seg_end)
+    g = _gate(gate)
+    _check(lib.nvfp4_w4a4_gemm(a_codes.data_ptr(), a_scales.data_ptr(), a_gscale.data_ptr(), M, N, 2 * half_k,
+                               w_codes.data_ptr(), w_scales.data_ptr(), n_seg, seg, w_seg_gscale.data_ptr(),
+                               ctypes.byref(g) if g is not None else None, y.data_ptr(), _dtype_code(y), ldy,
+                               _stream(stream)))
+
+
+def nvfp4_w4a4_linear(x, gscale_in, gscale_out, w_codes, w_scales, seg_end, w_seg_gscale, y, gate=None,
+                      a_codes_out=None, a_scales_out=None, stream=None) -> None:
+    """The whole layer: quantize x, GEMM, epilogues."""
+    M, K, ldx = _rows(x, "x")
+    N = w_codes.shape[0]
+    _, _, ldy = _rows(y, "y")
+    seg, n_seg = _seg_array(seg_end)
+    g = _gate(gate)
+    _check(lib.nvfp4_w4a4_linear(x.data_ptr(), _dtype_code(x), M, K, ldx, _ptr(gscale_in), gscale_out.data_ptr(),
+                                 N, w_codes.data_ptr(), w_scales.data_ptr(), n_seg, seg, w_seg_gscale.data_ptr(),
+                                 ctypes.byref(g) if g is not None else None, y.data_ptr(), _dtype_code(y), ldy,
+                                 _ptr(a_codes_out), _ptr(a_scales_out), _stream(stream)))

@@ -1,0 +1,299 @@
+// C ABI of the NVFP4 W4A4 linear layer: host-side validation and dispatch.
+// Every check happens before anything is enqueued; no call synchronizes.
+#include "../../include/nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int32_t ok() {
+  g_last_error.clear();
+  return NVFP4_OK;
+}
+
+int32_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dtype_size(int32_t t) { return t == NVFP4_DTYPE_F32 ? 4 : 2; }
+
+bool valid_dtype(int32_t t) { return t == NVFP4_DTYPE_F32 || t == NVFP4_DTYPE_BF16; }
+
+// Device check: the kernels are built for gfx950 only.  Cached per device id.
+int32_t check_device() {
+  static std::mutex mu;
+  static int cached[64];   // 0 unknown, 1 ok, 2 bad
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(NVFP4_ERR_DEVICE, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (cached[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    cached[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+  }
+  if (cached[dev] != 1) return fail(NVFP4_ERR_DEVICE, "current device is not gfx950 (MI355X)");
+  return NVFP4_OK;
+}
+
+int32_t check_x(const void* x, int32_t dt, int64_t rows, int64_t K, int64_t ld, const char* name) {
+  if (!x) return fail(NVFP4_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!valid_dtype(dt)) return fail(NVFP4_ERR_UNSUPPORTED, "%s dtype %d is not F32 or BF16", name, dt);
+  if (rows <= 0 || K <= 0) return fail(NVFP4_ERR_INVALID_ARG, "%s shape must be positive (rows=%lld K=%lld)", name,
+                                       (long long)rows, (long long)K);
+  if (K % 16) return fail(NVFP4_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
+  if (ld < K) return fail(NVFP4_ERR_INVALID_ARG, "ld%s=%lld < K=%lld", name, (long long)ld, (long long)K);
+  if (!aligned16(x) || (ld * (int64_t)dtype_size(dt)) % 16)
+    return fail(NVFP4_ERR_UNSUPPORTED, "%s must be 16-byte aligned with 16-byte aligned rows", name);
+  if (K / 8 > 0xFFFFFFFFll) return fail(NVFP4_ERR_UNSUPPORTED, "K too large");
+  return NVFP4_OK;
+}
+
+int32_t check_packed(const uint8_t* codes, const uint8_t* scales, const char* name) {
+  if (!codes || !scales) return fail(NVFP4_ERR_INVALID_ARG, "%s codes/scales pointer is NULL", name);
+  if (!aligned16(codes) || !aligned16(scales))
+    return fail(NVFP4_ERR_UNSUPPORTED, "%s codes/scales must be 16-byte aligned", name);
+  return NVFP4_OK;
+}
+
+int32_t build_seg(int32_t n_seg, const int64_t* seg_end, int64_t N, const float* scales_or_null,
+                  nvfp4::SegTable* out) {
+  if (n_seg < 1 || n_seg > NVFP4_MAX_SEGMENTS)
+    return fail(NVFP4_ERR_INVALID_ARG, "n_seg=%d outside [1, %d]", n_seg, NVFP4_MAX_SEGMENTS);
+  if (!seg_end) return fail(NVFP4_ERR_INVALID_ARG, "seg_end is NULL");
+  std::memset(out, 0, sizeof(*out));
+  out->n = n_seg;
+  int64_t prev = 0;
+  for (int i = 0; i < n_seg; ++i) {
+    if (seg_end[i] <= prev)
+      return fail(NVFP4_ERR_INVALID_ARG, "seg_end must be strictly increasing and positive (seg_end[%d]=%lld)", i,
+                  (long long)seg_end[i]);
+    prev = seg_end[i];
+    out->end[i] = seg_end[i];
+    if (scales_or_null) {
+      const float v = scales_or_null[i];
+      if (!std::isfinite(v) || v < 0.0f)
+        return fail(NVFP4_ERR_INVALID_ARG, "segment scale %d is not finite and >= 0", i);
+      out->scale[i] = v;
+    }
+  }
+  if (prev != N)
+    return fail(NVFP4_ERR_INVALID_ARG, "seg_end[last]=%lld must equal N=%lld", (long long)prev, (long long)N);
+  return NVFP4_OK;
+}
+
+int32_t check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                          int32_t n_seg, const int64_t* seg_end, const float* w_seg_gscale,
+                          const nvfp4_gate_params* gate, const void* y, int32_t y_dtype, int64_t ldy,
+                          nvfp4::GemmArgs* g) {
+  if (M <= 0 || N <= 0 || K <= 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "M, N, K must be positive (M=%lld N=%lld K=%lld)", (long long)M,
+                (long long)N, (long long)K);
+  if (K % 16) return fail(NVFP4_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
+  int32_t st = check_packed(w_codes, w_scales, "w");
+  if (st) return st;
+  if (!w_seg_gscale) return fail(NVFP4_ERR_INVALID_ARG, "w_seg_gscale is NULL");
+  if (!y) return fail(NVFP4_ERR_INVALID_ARG, "y is NULL");
+  if (!valid_dtype(y_dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "y dtype %d is not F32 or BF16", y_dtype);
+  if (ldy < N) return fail(NVFP4_ERR_INVALID_ARG, "ldy=%lld < N=%lld", (long long)ldy, (long long)N);
+  if (!aligned16(y)) return fail(NVFP4_ERR_UNSUPPORTED, "y must be 16-byte aligned");
+  st = build_seg(n_seg, seg_end, N, nullptr, &g->seg);
+  if (st) return st;
+  g->gate = nvfp4::GateArgs{0, nullptr, nullptr};
+  if (gate) {
+    if (gate->n_heads <= 0) return fail(NVFP4_ERR_INVALID_ARG, "gate n_heads must be positive");
+    if (N != 2 * (int64_t)gate->n_heads)
+      return fail(NVFP4_ERR_INVALID_ARG, "gate epilogue needs N == 2*n_heads (N=%lld, n_heads=%d)", (long long)N,
+                  gate->n_heads);
+    if (y_dtype != NVFP4_DTYPE_F32) return fail(NVFP4_ERR_INVALID_ARG, "gate epilogue needs y_dtype F32");
+    if (!gate->A_log || !gate->dt_bias) return fail(NVFP4_ERR_INVALID_ARG, "gate A_log/dt_bias is NULL");
+    g->gate = nvfp4::GateArgs{gate->n_heads, gate->A_log, gate->dt_bias};
+  }
+  g->M = M;
+  g->N = N;
+  g->K = K;
+  g->w_codes = w_codes;
+  g->w_scales = w_scales;
+  g->w_seg_gscale = w_seg_gscale;
+  g->y = const_cast<void*>(y);
+  g->y_type = y_dtype == NVFP4_DTYPE_F32 ? nvfp4::OutType::F32 : nvfp4::OutType::BF16;
+  g->ldy = ldy;
+  return NVFP4_OK;
+}
+
+nvfp4::InType in_type(int32_t dt) { return dt == NVFP4_DTYPE_F32 ? nvfp4::InType::F32 : nvfp4::InType::BF16; }
+
+// Enqueue activation quantization (validated arguments).
+hipError_t enqueue_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             const float* gscale_in, uint8_t* codes, uint8_t* scales, float* gscale_out,
+                             hipStream_t s) {
+  nvfp4::SegTable one{};
+  one.n = 1;
+  one.end[0] = M;
+  hipError_t e;
+  const float* gvec;
+  if (gscale_in) {
+    e = nvfp4::launch_copy_scalar(gscale_in, gscale_out, s);
+    if (e != hipSuccess) return e;
+    gvec = gscale_in;
+  } else {
+    e = nvfp4::launch_fill(gscale_out, 1, nullptr, s);
+    if (e != hipSuccess) return e;
+    e = nvfp4::launch_amax_gscale(x, in_type(x_dtype), M, K, ldx, gscale_out, s);
+    if (e != hipSuccess) return e;
+    gvec = gscale_out;
+  }
+  return nvfp4::launch_quant_rows(x, in_type(x_dtype), M, K, ldx, gvec, one, codes, scales, s);
+}
+
+// The fused decode GEMV holds x as f16 in LDS: M * K * 2 bytes.
+constexpr int64_t kGemvMaxM = 8;
+constexpr int64_t kGemvLdsBudget = 56 * 1024;
+
+bool gemv_fits(int64_t M, int64_t K) {
+  return M <= kGemvMaxM && K % 128 == 0 && M * K * 2 <= kGemvLdsBudget;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char* nvfp4_last_error(void) { return g_last_error.c_str(); }
+
+int32_t nvfp4_quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                           const float* gscale_in, uint8_t* codes, uint8_t* scales, float* gscale_out,
+                           void* stream) {
+  int32_t st = check_x(x, x_dtype, M, K, ldx, "x");
+  if (st) return st;
+  st = check_packed(codes, scales, "activation");
+  if (st) return st;
+  if (!gscale_out) return fail(NVFP4_ERR_INVALID_ARG, "gscale_out is NULL");
+  st = check_device();
+  if (st) return st;
+  return hip_status(enqueue_quant_act(x, x_dtype, M, K, ldx, gscale_in, codes, scales, gscale_out,
+                                      static_cast<hipStream_t>(stream)),
+                    "nvfp4_quantize_act launch");
+}
+
+int32_t nvfp4_pack_weight(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw, int32_t n_seg,
+                          const int64_t* seg_end, const float* seg_gscale_in, uint8_t* codes, uint8_t* scales,
+                          float* seg_gscale_out, void* stream) {
+  int32_t st = check_x(w, w_dtype, N, K, ldw, "w");
+  if (st) return st;
+  st = check_packed(codes, scales, "weight");
+  if (st) return st;
+  if (!seg_gscale_out) return fail(NVFP4_ERR_INVALID_ARG, "seg_gscale_out is NULL");
+  nvfp4::SegTable seg;
+  st = build_seg(n_seg, seg_end, N, seg_gscale_in, &seg);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (seg_gscale_in) {
+    e = nvfp4::launch_fill(seg_gscale_out, n_seg, &seg, s);
+  } else {
+    e = nvfp4::launch_fill(seg_gscale_out, n_seg, nullptr, s);
+    int64_t start = 0;
+    for (int i = 0; i < n_seg && e == hipSuccess; ++i) {
+      const char* base = static_cast<const char*>(w) + start * ldw * (int64_t)dtype_size(w_dtype);
+      e = nvfp4::launch_amax_gscale(base, in_type(w_dtype), seg.end[i] - start, K, ldw, seg_gscale_out + i, s);
+      start = seg.end[i];
+    }
+  }
+  if (e == hipSuccess) e = nvfp4::launch_quant_rows(w, in_type(w_dtype), N, K, ldw, seg_gscale_out, seg, codes, scales, s);
+  return hip_status(e, "nvfp4_pack_weight launch");
+}
+
+int32_t nvfp4_w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale, int64_t M,
+                        int64_t N, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales, int32_t n_seg,
+                        const int64_t* seg_end, const float* w_seg_gscale, const nvfp4_gate_params* gate, void* y,
+                        int32_t y_dtype, int64_t ldy, void* stream) {
+  nvfp4::GemmArgs g{};
+  int32_t st = check_packed(a_codes, a_scales, "activation");
+  if (st) return st;
+  if (!a_gscale) return fail(NVFP4_ERR_INVALID_ARG, "a_gscale is NULL");
+  st = check_gemm_common(M, N, K, w_codes, w_scales, n_seg, seg_end, w_seg_gscale, gate, y, y_dtype, ldy, &g);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  g.a_codes = a_codes;
+  g.a_scales = a_scales;
+  g.a_gscale = a_gscale;
+  return hip_status(nvfp4::launch_gemm_tiled(g, static_cast<hipStream_t>(stream)), "nvfp4_w4a4_gemm launch");
+}
+
+int32_t nvfp4_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, const float* gscale_in,
+                          float* gscale_out, int64_t N, const uint8_t* w_codes, const uint8_t* w_scales,
+                          int32_t n_seg, const int64_t* seg_end, const float* w_seg_gscale,
+                          const nvfp4_gate_params* gate, void* y, int32_t y_dtype, int64_t ldy, uint8_t* a_codes_out,
+                          uint8_t* a_scales_out, void* stream) {
+  int32_t st = check_x(x, x_dtype, M, K, ldx, "x");
+  if (st) return st;
+  if (!gscale_out) return fail(NVFP4_ERR_INVALID_ARG, "gscale_out is NULL");
+  if ((a_codes_out == nullptr) != (a_scales_out == nullptr))
+    return fail(NVFP4_ERR_INVALID_ARG, "a_codes_out and a_scales_out must both be given or both be NULL");
+  if (a_codes_out) {
+    st = check_packed(a_codes_out, a_scales_out, "activation");
+    if (st) return st;
+  }
+  nvfp4::GemmArgs g{};
+  st = check_gemm_common(M, N, K, w_codes, w_scales, n_seg, seg_end, w_seg_gscale, gate, y, y_dtype, ldy, &g);
+  if (st) return st;
+  const bool fused_gemv = gemv_fits(M, K);
+  if (!fused_gemv && !a_codes_out)
+    return fail(NVFP4_ERR_INVALID_ARG,
+                "this shape (M=%lld, N=%lld, K=%lld) runs in two stages and needs a_codes_out/a_scales_out",
+                (long long)M, (long long)N, (long long)K);
+  st = check_device();
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fused_gemv) {
+    nvfp4::GemvArgs p{};
+    p.x = x;
+    p.x_type = in_type(x_dtype);
+    p.ldx = ldx;
+    p.gscale_in = gscale_in;
+    p.gscale_out = gscale_out;
+    p.a_codes_out = a_codes_out;
+    p.a_scales_out = a_scales_out;
+    p.g = g;
+    return hip_status(nvfp4::launch_gemv_fused(p, s), "nvfp4_w4a4_linear (fused decode) launch");
+  }
+  hipError_t e = enqueue_quant_act(x, x_dtype, M, K, ldx, gscale_in, a_codes_out, a_scales_out, gscale_out, s);
+  if (e != hipSuccess) return hip_status(e, "nvfp4_w4a4_linear quantize launch");
+  g.a_codes = a_codes_out;
+  g.a_scales = a_scales_out;
+  g.a_gscale = gscale_out;
+  return hip_status(nvfp4::launch_gemm_tiled(g, s), "nvfp4_w4a4_linear gemm launch");
+}
+
+}  // extern "C"

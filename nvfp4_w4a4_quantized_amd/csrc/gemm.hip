@@ -1,0 +1,383 @@
+// Block-scaled W4A4 GEMM kernels for gfx950.
+//
+// Operands stay packed (4-bit codes + E4M3 block scales) in HBM and LDS.  Each lane
+// decodes its MFMA operand in registers: 8 codes (one dword) -> f16 e2m1 values by the
+// hardware fp4 conversion, times the block scale as f16 (exact: the product has <= 6
+// significant bits and lies in [2^-10, 2688]).  f16 x f16 products are exact in
+// fp32; MFMA accumulates in fp32.  The epilogue multiplies column n by
+// g_a * g_w[segment(n)] (the per-segment global-scale repair for fused GEMMs over
+// per-module-calibrated weights: "Why Gated DeltaNet Survives 4-Bit Quantization"
+// review page, strengths paragraph / the paper's section 6) and optionally applies
+// the GDN gates of Eq. 1 (same page, mechanism step 2).
+//
+// K-permutation.  A lane loads 16 contiguous bytes (32 elements) of its row; MFMA
+// step t uses dword t of them.  Both operands use the same permutation of k, so the
+// sum over k is unchanged, and every 8-element group a lane feeds to one MFMA lies
+// inside one 16-element scale block.
+#include "launch.hpp"
+#include "nvfp4_device.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+__device__ __forceinline__ int seg_of_col(const SegTable& seg, int64_t n) {
+  int s = 0;
+  while (s + 1 < seg.n && n >= seg.end[s]) ++s;
+  return s;
+}
+
+__device__ __forceinline__ float softplus_f32(float z) {
+  return __builtin_fmaxf(z, 0.0f) + log1pf(expf(-__builtin_fabsf(z)));
+}
+
+__device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+// Epilogue for one output element: alpha scaling, optional gate, store.
+__device__ __forceinline__ void store_out(const GemmArgs& a, int64_t m, int64_t n, float acc, float alpha) {
+  float v = acc * alpha;
+  if (a.gate.n_heads > 0) {
+    const int64_t H = a.gate.n_heads;
+    if (n < H) {
+      const float z = v + a.gate.dt_bias[n];
+      v = -expf(a.gate.A_log[n]) * softplus_f32(z);
+    } else {
+      v = sigmoid_f32(v);
+    }
+  }
+  if (a.y_type == OutType::BF16) {
+    reinterpret_cast<uint16_t*>(a.y)[m * a.ldy + n] = (uint16_t)f32_to_bf16_bits(v);
+  } else {
+    reinterpret_cast<float*>(a.y)[m * a.ldy + n] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Tiled GEMM: 128 x 128 output tile per workgroup, BK = 64, 4 waves of 64 x 64,
+// MFMA 32x32x16 f16.  Packed tiles are staged through LDS (codes 4 KiB + scales
+// 512 B per operand per K step) with a register prefetch of the next step.
+// ---------------------------------------------------------------------------------
+constexpr int TBM = 128, TBN = 128, TBK = 64;
+
+struct TileRegs {
+  u32x4 ca, cw;     // 16 bytes of codes for A and W
+  uint32_t sc;      // 4 scale bytes (A for threads < 128, W otherwise)
+};
+
+template <bool ALIGNED>
+__device__ __forceinline__ u32x4 load_codes16(const uint8_t* base, int64_t row, int64_t rows, int64_t K,
+                                              int64_t k0, int h) {
+  u32x4 r = {0u, 0u, 0u, 0u};
+  if (row >= rows) return r;
+  const int64_t kk = k0 + 32 * h;             // first element of this half
+  const uint8_t* p = base + row * (K >> 1) + (kk >> 1);
+  if constexpr (ALIGNED) {
+    r = *reinterpret_cast<const u32x4*>(p);
+  } else {
+    // K % 64 != 0: load 8 bytes (16 elements) at a time, only inside the row
+    if (kk < K) {
+      const uint2 lo = *reinterpret_cast<const uint2*>(p);
+      r[0] = lo.x; r[1] = lo.y;
+    }
+    if (kk + 16 < K) {
+      const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
+      r[2] = hi.x; r[3] = hi.y;
+    }
+  }
+  return r;
+}
+
+template <bool ALIGNED>
+__device__ __forceinline__ uint32_t load_scales4(const uint8_t* base, int64_t row, int64_t rows, int64_t K,
+                                                 int64_t k0) {
+  if (row >= rows) return 0u;
+  const int64_t kb = K >> 4;
+  const uint8_t* p = base + row * kb + (k0 >> 4);
+  if constexpr (ALIGNED) {
+    return *reinterpret_cast<const uint32_t*>(p);
+  } else {
+    uint32_t r = 0;
+    for (int j = 0; j < 4; ++j)
+      if ((k0 >> 4) + j < kb) r |= (uint32_t)p[j] << (8 * j);
+    return r;
+  }
+}
+
+template <bool ALIGNED>
+__global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
+  __shared__ u32x4 lds_ca[2][TBM];
+  __shared__ u32x4 lds_cw[2][TBN];
+  __shared__ uint32_t lds_sa[TBM];
+  __shared__ uint32_t lds_sw[TBN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, li = lane & 31;
+
+  // tile order: groups of 8 row-tiles sweep the column tiles (L2 reuse of W)
+  const int64_t tiles_m = (a.M + TBM - 1) / TBM;
+  const int64_t tiles_n = (a.N + TBN - 1) / TBN;
+  const int64_t pid = blockIdx.x;
+  const int64_t group = 8;
+  const int64_t per_group = group * tiles_n;
+  const int64_t gid = pid / per_group;
+  const int64_t first_m = gid * group;
+  const int64_t gsize = (tiles_m - first_m) < group ? (tiles_m - first_m) : group;
+  const int64_t bm = first_m + (pid % per_group) % gsize;
+  const int64_t bn = (pid % per_group) / gsize;
+  const int64_t m0 = bm * TBM, n0 = bn * TBN;
+
+  // loader roles: thread -> (row, half) for codes; threads < 128 load A scales, others W
+  const int lrow = tid >> 1, lh = tid & 1;
+  const int srow = tid & 127;
+  const bool s_is_a = tid < 128;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto gload = [&](int64_t k0) {
+    TileRegs t;
+    t.ca = load_codes16<ALIGNED>(a.a_codes, m0 + lrow, a.M, a.K, k0, lh);
+    t.cw = load_codes16<ALIGNED>(a.w_codes, n0 + lrow, a.N, a.K, k0, lh);
+    t.sc = s_is_a ? load_scales4<ALIGNED>(a.a_scales, m0 + srow, a.M, a.K, k0)
+                  : load_scales4<ALIGNED>(a.w_scales, n0 + srow, a.N, a.K, k0);
+    return t;
+  };
+
+  TileRegs cur = gload(0);
+  for (int64_t k0 = 0; k0 < a.K; k0 += TBK) {
+    lds_ca[lh][lrow] = cur.ca;
+    lds_cw[lh][lrow] = cur.cw;
+    if (s_is_a) lds_sa[srow] = cur.sc; else lds_sw[srow] = cur.sc;
+    __syncthreads();
+    if (k0 + TBK < a.K) cur = gload(k0 + TBK);
+
+    f16x8 A[2][4], B[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = wm * 64 + i * 32 + li;
+      const u32x4 c = lds_ca[h][r];
+      const uint32_t s = lds_sa[r] >> (16 * h);
+      const f16x2 s0 = scale_f16x2(s & 0xFFu), s1 = scale_f16x2((s >> 8) & 0xFFu);
+      A[i][0] = decode8_f16(c[0], s0);
+      A[i][1] = decode8_f16(c[1], s0);
+      A[i][2] = decode8_f16(c[2], s1);
+      A[i][3] = decode8_f16(c[3], s1);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = wn * 64 + j * 32 + li;
+      const u32x4 c = lds_cw[h][r];
+      const uint32_t s = lds_sw[r] >> (16 * h);
+      const f16x2 s0 = scale_f16x2(s & 0xFFu), s1 = scale_f16x2((s >> 8) & 0xFFu);
+      B[j][0] = decode8_f16(c[0], s0);
+      B[j][1] = decode8_f16(c[1], s0);
+      B[j][2] = decode8_f16(c[2], s1);
+      B[j][3] = decode8_f16(c[3], s1);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i][t], B[j][t], acc[i][j], 0, 0, 0);
+    __syncthreads();
+  }
+
+  const float ga = *a.a_gscale;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = n0 + wn * 64 + j * 32 + li;
+    if (n >= a.N) continue;
+    const float alpha = ga * a.w_seg_gscale[seg_of_col(a.seg, n)];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < a.M) store_out(a, m, n, acc[i][j][r], alpha);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Fused decode GEMV (M <= 8).  One workgroup = 64 weight rows, 8 waves: wave w takes
+// rows 16*(w&3) .. +15 and half of K.  Prologue: the workgroup quantizes all of x
+// (M x K) into LDS as f16 dequantized values (e2m1 * s), using the same exact
+// quantizer as the stand-alone kernel.  Main loop: MFMA 16x16x32 f16 with the 16
+// weight rows as the A operand and the M tokens (padded to 16 columns) as B.
+// ---------------------------------------------------------------------------------
+constexpr int GV_ROWS = 64;
+constexpr int GV_THREADS = 512;
+
+__device__ __forceinline__ float dpp_swap_adjacent(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+template <InType T>
+__device__ __forceinline__ void gv_load8(const void* base, int64_t off, float v[8]) {
+  if constexpr (T == InType::BF16) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(q[i] << 16);
+      v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float* p = reinterpret_cast<const float*>(base) + off;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = x0[i]; v[4 + i] = x1[i]; }
+  }
+}
+
+template <InType T>
+__global__ __launch_bounds__(GV_THREADS) void k_gemv_fused(GemvArgs p) {
+  extern __shared__ __attribute__((aligned(16))) _Float16 xs[];   // [M][K] f16
+  __shared__ float red_g[GV_THREADS / 64];
+  __shared__ f32x4 red_acc[4][64];
+  const GemmArgs& a = p.g;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t M = a.M, K = a.K, N = a.N;
+  const uint32_t chunks_per_row = (uint32_t)(K >> 3);
+  const uint32_t total_chunks = (uint32_t)M * chunks_per_row;
+  const uint32_t iters = (total_chunks + GV_THREADS - 1) / GV_THREADS;
+
+  // ---- global scale (dynamic mode: amax over the whole of x)
+  float g;
+  if (p.gscale_in) {
+    g = *p.gscale_in;
+  } else {
+    float am = 0.0f;
+    for (uint32_t it = 0; it < iters; ++it) {
+      const uint32_t c = it * GV_THREADS + tid;
+      if (c < total_chunks) {
+        const uint32_t row = c / chunks_per_row;
+        const uint32_t col = (c - row * chunks_per_row) * 8u;
+        float v[8];
+        gv_load8<T>(p.x, (int64_t)row * p.ldx + col, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) am = __builtin_fmaxf(am, __builtin_fabsf(v[i]));
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) am = __builtin_fmaxf(am, __shfl_xor(am, off));
+    if (lane == 0) red_g[wave] = am;
+    __syncthreads();
+    am = red_g[0];
+#pragma unroll
+    for (int i = 1; i < GV_THREADS / 64; ++i) am = __builtin_fmaxf(am, red_g[i]);
+    g = global_scale_from_amax(am);
+  }
+  if (blockIdx.x == 0 && tid == 0 && p.gscale_out) *p.gscale_out = g;
+
+  // ---- quantize x into LDS (f16 of e2m1 * s); workgroup 0 also writes the codes
+  const bool write_codes = blockIdx.x == 0 && p.a_codes_out != nullptr;
+  for (uint32_t it = 0; it < iters; ++it) {
+    const uint32_t c = it * GV_THREADS + tid;
+    const bool valid = c < total_chunks;
+    uint32_t row = 0, col = 0;
+    float v[8];
+    if (valid) {
+      row = c / chunks_per_row;
+      col = (c - row * chunks_per_row) * 8u;
+      gv_load8<T>(p.x, (int64_t)row * p.ldx + col, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    float am = __builtin_fabsf(v[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) am = __builtin_fmaxf(am, __builtin_fabsf(v[i]));
+    am = __builtin_fmaxf(am, dpp_swap_adjacent(am));
+    const uint32_t sb = block_scale_byte(am, g);
+    const uint32_t w = quant8(v, sb, g);
+    if (valid) {
+      const f16x8 d = decode8_f16(w, scale_f16x2(sb));
+      *reinterpret_cast<f16x8*>(xs + (int64_t)row * K + col) = d;
+      if (write_codes) {
+        *reinterpret_cast<uint32_t*>(p.a_codes_out + (int64_t)row * (K >> 1) + (col >> 1)) = w;
+        if ((tid & 1) == 0) p.a_scales_out[(int64_t)row * (K >> 4) + (col >> 4)] = (uint8_t)sb;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- main loop
+  const int sub = wave & 3, khalf = wave >> 2;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int64_t wrow = (int64_t)blockIdx.x * GV_ROWS + sub * 16 + r16;   // weight row of this lane
+  const bool row_ok = wrow < N;
+  const int64_t n_chunks = K >> 7;                                      // 128 elements per chunk
+  const int64_t c_begin = khalf ? n_chunks / 2 : 0;
+  const int64_t c_end = khalf ? n_chunks : n_chunks / 2;
+  const uint8_t* wc = a.w_codes + (row_ok ? wrow : 0) * (K >> 1);
+  const uint8_t* wsc = a.w_scales + (row_ok ? wrow : 0) * (K >> 4);
+  const int xtok = r16 % (int)M;
+  const _Float16* xrow = xs + (int64_t)xtok * K;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t c = c_begin; c < c_end; ++c) {
+    const u32x4 codes = row_ok ? *reinterpret_cast<const u32x4*>(wc + c * 64 + 16 * q) : u32x4{0u, 0u, 0u, 0u};
+    const uint32_t s2 = row_ok ? *reinterpret_cast<const uint16_t*>(wsc + c * 8 + 2 * q) : 0u;
+    const f16x2 s0 = scale_f16x2(s2 & 0xFFu), s1 = scale_f16x2(s2 >> 8);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const f16x8 wa = decode8_f16(codes[t], t < 2 ? s0 : s1);
+      const f16x8 xb = *reinterpret_cast<const f16x8*>(xrow + c * 128 + 32 * q + 8 * t);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, xb, acc, 0, 0, 0);
+    }
+  }
+  if (khalf) red_acc[sub][lane] = acc;
+  __syncthreads();
+  if (!khalf) {
+    const f32x4 o = red_acc[sub][lane];
+    const float ga = g;
+    const int tok = r16;               // D column = token
+    if (tok < M) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t n = (int64_t)blockIdx.x * GV_ROWS + sub * 16 + 4 * q + r;
+        if (n < N) {
+          const float alpha = ga * a.w_seg_gscale[seg_of_col(a.seg, n)];
+          store_out(a, tok, n, acc[r] + o[r], alpha);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) {
+  const int64_t tiles = ((a.M + TBM - 1) / TBM) * ((a.N + TBN - 1) / TBN);
+  if (a.K % 64 == 0)
+    hipLaunchKernelGGL(k_gemm_tiled<true>, dim3((unsigned)tiles), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_gemm_tiled<false>, dim3((unsigned)tiles), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+size_t gemv_lds_bytes(int64_t M, int64_t K) { return (size_t)M * (size_t)K * 2; }
+
+hipError_t launch_gemv_fused(const GemvArgs& p, hipStream_t s) {
+  const unsigned grid = (unsigned)((p.g.N + GV_ROWS - 1) / GV_ROWS);
+  const size_t lds = gemv_lds_bytes(p.g.M, p.g.K);
+  if (p.x_type == InType::BF16)
+    hipLaunchKernelGGL(k_gemv_fused<InType::BF16>, dim3(grid), dim3(GV_THREADS), lds, s, p);
+  else
+    hipLaunchKernelGGL(k_gemv_fused<InType::F32>, dim3(grid), dim3(GV_THREADS), lds, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

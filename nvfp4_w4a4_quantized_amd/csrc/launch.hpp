@@ -1,0 +1,68 @@
+// Internal launch interface between the C ABI (abi.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kMaxSeg = 64;
+
+// Segment table passed to kernels by value.  end[i] = one past the last row
+// (output column) of segment i; scale[i] = host-given calibrated scale (static mode).
+struct SegTable {
+  int32_t n;
+  int32_t pad;
+  int64_t end[kMaxSeg];
+  float scale[kMaxSeg];
+};
+
+struct GateArgs {
+  int32_t n_heads;         // 0 = no gate epilogue
+  const float* A_log;
+  const float* dt_bias;
+};
+
+enum class InType : int { F32 = 0, BF16 = 1 };
+enum class OutType : int { F32 = 0, BF16 = 1 };
+
+// quant.hip
+hipError_t launch_fill(float* dst, int n, const SegTable* vals_or_null, hipStream_t s);
+hipError_t launch_amax_gscale(const void* x, InType t, int64_t rows, int64_t K, int64_t ld,
+                              float* gscale_out, hipStream_t s);
+hipError_t launch_quant_rows(const void* x, InType t, int64_t rows, int64_t K, int64_t ld,
+                             const float* gvec, const SegTable& seg,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_copy_scalar(const float* src, float* dst, hipStream_t s);
+
+// gemm.hip
+struct GemmArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* a_gscale;
+  int64_t M, N, K;
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  const float* w_seg_gscale;
+  SegTable seg;
+  GateArgs gate;
+  void* y;
+  OutType y_type;
+  int64_t ldy;
+};
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s);
+
+// Fused decode GEMV (M <= 8): quantizes x itself, optionally writes the codes.
+struct GemvArgs {
+  const void* x;
+  InType x_type;
+  int64_t ldx;
+  const float* gscale_in;      // NULL = dynamic
+  float* gscale_out;
+  uint8_t* a_codes_out;        // optional
+  uint8_t* a_scales_out;       // optional
+  GemmArgs g;                  // a_codes/a_scales/a_gscale unused
+};
+hipError_t launch_gemv_fused(const GemvArgs& a, hipStream_t s);
+
+}  // namespace nvfp4

@@ -1,0 +1,122 @@
+"""The C-ABI library builds, loads and exports every symbol include/nvfp4.h declares,
+and its host-side validation rejects bad arguments before touching the GPU.
+CPU only: no compute call reaches a kernel here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+@pytest.fixture(scope="module")
+def nv():
+    lib_path = os.path.join(ROOT, "nvfp4_w4a4_quantized_amd", "libnvfp4.so")
+    if not os.path.exists(lib_path):
+        import __graft_entry__
+        __graft_entry__.build()
+    import nvfp4_w4a4_quantized_amd as nvmod
+    return nvmod
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"NVFP4_API\s+[\w\s\*]+?\b(nvfp4_\w+)\s*\(", src)))
+
+
+def test_header_declarations_are_exported(nv):
+    names = _declared()
+    assert names == sorted(nv.EXPORTED)
+    for n in names:
+        assert hasattr(nv.lib, n), n
+    ver = int(re.search(r"#define NVFP4_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert nv.nvfp4_abi_version() == ver
+
+
+FAKE = ctypes.c_void_p(1 << 20)        # a 16-byte aligned non-null address, never dereferenced
+FAKE_ODD = ctypes.c_void_p((1 << 20) + 4)
+
+
+def _q(nv, x=FAKE, dt=1, M=4, K=64, ld=64, gin=None, codes=FAKE, scales=FAKE, gout=FAKE):
+    return nv.lib.nvfp4_quantize_act(x, dt, M, K, ld, gin, codes, scales, gout, None)
+
+
+def test_quantize_act_validation(nv):
+    assert _q(nv, x=None) == nv.NVFP4_ERR_INVALID_ARG and "NULL" in nv.nvfp4_last_error()
+    assert _q(nv, K=60, ld=64) == nv.NVFP4_ERR_INVALID_ARG and "multiple of 16" in nv.nvfp4_last_error()
+    assert _q(nv, M=0) == nv.NVFP4_ERR_INVALID_ARG
+    assert _q(nv, M=-3) == nv.NVFP4_ERR_INVALID_ARG
+    assert _q(nv, ld=48) == nv.NVFP4_ERR_INVALID_ARG
+    assert _q(nv, dt=7) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(nv, x=FAKE_ODD) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(nv, ld=68) == nv.NVFP4_ERR_UNSUPPORTED            # bf16 rows not 16-byte aligned
+    assert _q(nv, codes=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert _q(nv, gout=None) == nv.NVFP4_ERR_INVALID_ARG
+
+
+def _segs(vals):
+    return (ctypes.c_int64 * len(vals))(*vals), len(vals)
+
+
+def test_pack_weight_validation(nv):
+    def call(seg_vals, gin=None, N=96):
+        seg, n = _segs(seg_vals)
+        g = None if gin is None else (ctypes.c_float * len(gin))(*gin)
+        return nv.lib.nvfp4_pack_weight(FAKE, 0, N, 64, 64, n, seg, g, FAKE, FAKE, FAKE, None)
+    assert call([48, 48, 96]) == nv.NVFP4_ERR_INVALID_ARG and "increasing" in nv.nvfp4_last_error()
+    assert call([50]) == nv.NVFP4_ERR_INVALID_ARG and "equal N" in nv.nvfp4_last_error()
+    assert call([0, 96]) == nv.NVFP4_ERR_INVALID_ARG
+    assert call([48, 96], gin=[1.0, float("nan")]) == nv.NVFP4_ERR_INVALID_ARG
+    assert call([48, 96], gin=[1.0, -2.0]) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(list(range(1, 66)), N=65) == nv.NVFP4_ERR_INVALID_ARG      # more than 64 segments
+    seg, n = _segs([96])
+    assert nv.lib.nvfp4_pack_weight(FAKE, 0, 96, 64, 64, 0, seg, None, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_INVALID_ARG
+    assert nv.lib.nvfp4_pack_weight(FAKE, 0, 96, 64, 64, 1, None, None, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_INVALID_ARG
+
+
+def _gemm(nv, M=4, N=96, K=64, seg_vals=(48, 96), gate=None, y_dtype=1, ldy=96, y=FAKE, a=FAKE, ag=FAKE):
+    seg, n = _segs(list(seg_vals))
+    g = ctypes.byref(gate) if gate is not None else None
+    return nv.lib.nvfp4_w4a4_gemm(a, FAKE, ag, M, N, K, FAKE, FAKE, n, seg, FAKE, g, y, y_dtype, ldy, None)
+
+
+def test_gemm_validation(nv):
+    assert _gemm(nv, K=40) == nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(nv, N=0, seg_vals=(1,)) == nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(nv, ldy=50) == nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(nv, seg_vals=(48, 90)) == nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(nv, a=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(nv, ag=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(nv, y=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(nv, y_dtype=5) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _gemm(nv, y=FAKE_ODD) == nv.NVFP4_ERR_UNSUPPORTED
+    bad = nv.GateParams(40, FAKE.value, FAKE.value)            # N != 2 * n_heads
+    assert _gemm(nv, gate=bad, y_dtype=0) == nv.NVFP4_ERR_INVALID_ARG and "2*n_heads" in nv.nvfp4_last_error()
+    good = nv.GateParams(48, FAKE.value, FAKE.value)
+    assert _gemm(nv, gate=good, y_dtype=1) == nv.NVFP4_ERR_INVALID_ARG      # gate needs fp32 output
+    nul = nv.GateParams(48, None, FAKE.value)
+    assert _gemm(nv, gate=nul, y_dtype=0) == nv.NVFP4_ERR_INVALID_ARG
+
+
+def test_linear_validation(nv):
+    seg, n = _segs([4096])
+    # two-stage shape without workspace for the activation codes
+    st = nv.lib.nvfp4_w4a4_linear(FAKE, 1, 512, 256, 256, None, FAKE, 4096, FAKE, FAKE, n, seg, FAKE, None,
+                                  FAKE, 1, 4096, None, None, None)
+    assert st == nv.NVFP4_ERR_INVALID_ARG and "a_codes_out" in nv.nvfp4_last_error()
+    st = nv.lib.nvfp4_w4a4_linear(FAKE, 1, 4, 256, 256, None, FAKE, 4096, FAKE, FAKE, n, seg, FAKE, None,
+                                  FAKE, 1, 4096, FAKE, None, None)
+    assert st == nv.NVFP4_ERR_INVALID_ARG
+    st = nv.lib.nvfp4_w4a4_linear(FAKE, 1, 4, 256, 256, None, None, 4096, FAKE, FAKE, n, seg, FAKE, None,
+                                  FAKE, 1, 4096, None, None, None)
+    assert st == nv.NVFP4_ERR_INVALID_ARG
+
+
+def test_binding_rejects_wrong_dtype(nv):
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.float16)
+    with pytest.raises(nv.Nvfp4Error):
+        nv.nvfp4_quantize_act(x, None, x, x, x)

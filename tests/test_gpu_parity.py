@@ -1,0 +1,296 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same
+seeded inputs.  Codes, scale bytes and global scales must be bit-exact; GEMM and
+gate outputs must be within 1e-3 relative Frobenius error and within the
+per-element bound computed by the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import nvfp4 as O
+from synth import workloads as W
+from tests import paritylib as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import nvfp4_w4a4_quantized_amd as nvmod
+    return nvmod
+
+
+def _x_inputs(wl):
+    xv = W.x_values_f32(wl)
+    return xv, P.dev_x(xv, wl.data.get("x_bf16"))
+
+
+# ----------------------------------------------------------------------------- quantization
+
+@pytest.mark.parametrize("name,M", [
+    ("tiny_linear_64x128x256", None),
+    ("decode_gemv_4x16384x5120", None),
+    ("gdn_in_proj_8192x16384x5120", 203),
+    ("gdn_gates_32768x96x5120", 130),
+    ("mlp_gate_up_32768x34816x5120", 77),
+])
+@pytest.mark.parametrize("mode", ["dynamic", "static"])
+def test_quantize_act_matches_oracle(nv, name, M, mode):
+    wl = W.generate(name, M=M, with_weight=False)
+    xv, xt = _x_inputs(wl)
+    x64 = P.x64_of(xv)
+    g_static = np.float32(0.0371) if mode == "static" else None
+    oc, os_, og = O.quantize_activation(x64, g_static)
+    gc, gs, gg = P.gpu_quantize(nv, xt, None if g_static is None else float(g_static))
+    assert gg == og, (gg, og)
+    P.assert_bytes_equal(gs, os_, "scales")
+    P.assert_bytes_equal(gc, oc, "codes")
+
+
+def _adversarial_inputs():
+    rows = []
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    rows.append([6.0] + mids + [-m for m in mids] + [0.0])       # E2M1 ties with s = 1
+    rows.append([6.375, 1.0, -0.0, 0.125] + [0.0] * 12)           # E4M3 tie 1.0625 -> 1.0
+    rows.append([0.0] * 8 + [-0.0] * 8)                           # zero block with -0
+    rows.append([1e-3, -1e-3, 6.0] + [0.0] * 13)                  # tiny values round to +-0
+    rows.append([3.0, -2.9990234375, 2.5, 0.5] * 4)               # values on and near grid points
+    rows.append([1e-30, -3e-31] + [0.0] * 14)                     # scale underflows to 0
+    rows.append([5e4, -4.9e4, 1.0, -1.0] * 4)                     # large values, static overflow
+    arr = np.array(rows, dtype=np.float32)
+    rng = np.random.default_rng(21)
+    rnd = (rng.standard_normal((5, 16)) * np.array([[1e-3], [1.0], [37.0], [1e4], [3e-5]])).astype(np.float32)
+    return np.concatenate([arr, rnd], axis=0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("g", [1.0, 0.0371, 2.0, 1e-5, 40.0, None])
+def test_quantize_adversarial(nv, dtype, g):
+    x = _adversarial_inputs()
+    x = np.tile(x, (1, 4))                                        # K = 64
+    if dtype == "bf16":
+        bits = W._to_bf16_bits(x)
+        xv = W.bf16_bits_to_f32(bits)
+        xt = P.dev_x(xv, bits)
+    else:
+        xv, xt = x, P.dev_x(x)
+    oc, os_, og = O.quantize_activation(P.x64_of(xv), None if g is None else np.float32(g))
+    gc, gs, gg = P.gpu_quantize(nv, xt, g)
+    assert gg == og
+    P.assert_bytes_equal(gs, os_, "scales")
+    P.assert_bytes_equal(gc, oc, "codes")
+
+
+def test_quantize_near_midpoints_dense(nv):
+    """Values placed exactly on and 1..3 fp32 ulps around every E2M1 midpoint under
+    non-trivial block scales: exercises the exact fix-up path."""
+    rng = np.random.default_rng(22)
+    g = np.float32(0.0173)
+    rows = []
+    for _ in range(64):
+        sb = int(rng.integers(0x20, 0x7F))
+        s = float(O.e4m3_value(sb))
+        blk = np.zeros(16, dtype=np.float64)
+        blk[0] = 6 * s * float(g)                                 # sets the block scale to s
+        mids = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], size=15)
+        vals = (mids * s * float(g)).astype(np.float32)
+        d = rng.integers(-3, 4, size=15)
+        vals = vals.view(np.int32) + d.astype(np.int32)
+        blk[1:] = vals.view(np.float32) * rng.choice([-1, 1], size=15)
+        rows.append(blk.astype(np.float32))
+    x = np.stack(rows)
+    x = np.tile(x, (1, 2))
+    oc, os_, og = O.quantize_activation(P.x64_of(x), g)
+    gc, gs, gg = P.gpu_quantize(nv, P.dev_x(x), float(g))
+    P.assert_bytes_equal(gs, os_, "scales")
+    P.assert_bytes_equal(gc, oc, "codes")
+
+
+def test_quantize_strided_rows_and_ragged(nv):
+    rng = np.random.default_rng(23)
+    for M, K in [(1, 16), (3, 48), (17, 272), (5, 528)]:
+        full = (rng.standard_normal((M, K + 32)) * 3).astype(np.float32)
+        xt = P.dev_x(full)[:, :K]                                 # ldx = K + 32
+        oc, os_, og = O.quantize_activation(P.x64_of(full[:, :K]))
+        gc, gs, gg = P.gpu_quantize(nv, xt)
+        assert gg == og
+        P.assert_bytes_equal(gs, os_, f"scales {M}x{K}")
+        P.assert_bytes_equal(gc, oc, f"codes {M}x{K}")
+
+
+def test_quantize_deterministic(nv):
+    wl = W.generate("gdn_in_proj_8192x16384x5120", M=512, with_weight=False)
+    _, xt = _x_inputs(wl)
+    a = P.gpu_quantize(nv, xt)
+    b = P.gpu_quantize(nv, xt)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+# ----------------------------------------------------------------------------- weight packing
+
+@pytest.mark.parametrize("seg_end,sigma,static", [
+    ([256, 512, 1280, 2048], [0.02, 0.04, 0.01, 0.08], False),
+    ([48, 96], [0.02, 0.02], False),
+    ([1024, 2048], [0.02, 0.08], True),
+    ([130], [0.02], False),
+])
+def test_pack_weight_matches_oracle(nv, seg_end, sigma, static):
+    rng = np.random.default_rng(31)
+    K = 512
+    parts, start = [], 0
+    for e, sg in zip(seg_end, sigma):
+        parts.append(rng.standard_normal((e - start, K)).astype(np.float32) * np.float32(sg))
+        start = e
+    w = np.concatenate(parts)
+    w64 = w.astype(np.float64)
+    gin = None
+    if static:
+        g0 = O.global_scale(O.tensor_amax(w64[:seg_end[0]]))
+        gin = [float(g0), float(np.float32(4) * g0)]
+    oc, os_, og = O.pack_weight(w64, seg_end, gin)
+    gc, gs, gg = P.gpu_pack(nv, P.dev_x(w), seg_end, gin)
+    assert np.array_equal(gg.cpu().numpy(), og)
+    P.assert_bytes_equal(gs.cpu().numpy(), os_, "weight scales")
+    P.assert_bytes_equal(gc.cpu().numpy(), oc, "weight codes")
+
+
+# ----------------------------------------------------------------------------- GEMM
+
+def _run_layer(nv, wl, use_linear, out_rows=None, seg_gscale=None, act_static=None):
+    """Pack W, quantize X, run the GEMM on the GPU; return everything the oracle check needs."""
+    xv, xt = _x_inputs(wl)
+    w = wl.data["w32"]
+    wt = P.dev_x(w)
+    wc, ws, wg = P.gpu_pack(nv, wt, wl.seg_end, seg_gscale)
+    M, N = xt.shape[0], w.shape[0]
+    y_dtype = torch.bfloat16 if wl.y_dtype == "bf16" else torch.float32
+    y = torch.empty((M, N), dtype=y_dtype, device="cuda")
+    gate = None
+    if wl.gate_heads:
+        gate = (torch.from_numpy(wl.data["A_log"]).cuda(), torch.from_numpy(wl.data["dt_bias"]).cuda())
+    gin = None if act_static is None else torch.tensor([act_static], dtype=torch.float32, device="cuda")
+    ac, as_ = nv.empty_packed(M, wl.K, "cuda")
+    gout = torch.empty(1, dtype=torch.float32, device="cuda")
+    if use_linear:
+        nv.nvfp4_w4a4_linear(xt, gin, gout, wc, ws, wl.seg_end, wg, y, gate=gate, a_codes_out=ac, a_scales_out=as_)
+    else:
+        nv.nvfp4_quantize_act(xt, gin, ac, as_, gout)
+        nv.nvfp4_w4a4_gemm(ac, as_, gout, wc, ws, wl.seg_end, wg, y, gate=gate)
+    torch.cuda.synchronize()
+    return dict(xv=xv, w=w, y=y, ac=ac.cpu().numpy(), as_=as_.cpu().numpy(), ag=np.float32(gout.item()),
+                wc=wc.cpu().numpy(), ws=ws.cpu().numpy(), wg=wg.cpu().numpy())
+
+
+def _oracle_side(wl, r, seg_gscale=None, act_static=None, rows=None, cols=None):
+    x64 = P.x64_of(r["xv"])
+    ac, as_, ag = O.quantize_activation(x64, None if act_static is None else np.float32(act_static))
+    w64 = r["w"].astype(np.float64)
+    wc, ws, wg = O.pack_weight(w64, wl.seg_end, seg_gscale)
+    assert ag == r["ag"] and np.array_equal(wg, r["wg"])
+    P.assert_bytes_equal(r["ac"], ac, "activation codes")
+    P.assert_bytes_equal(r["as_"], as_, "activation scales")
+    P.assert_bytes_equal(r["wc"], wc, "weight codes")
+    P.assert_bytes_equal(r["ws"], ws, "weight scales")
+    gate = (wl.data["A_log"], wl.data["dt_bias"]) if wl.gate_heads else None
+    return P.oracle_reference(ac, as_, ag, wc, ws, wl.seg_end, wg, wl.y_dtype, gate=gate, rows=rows, cols=cols)
+
+
+def _shrink(wl, N_seg_end=None, sigma=None, M=None, seed=0):
+    """Replace the weight by a smaller one with the same segment structure."""
+    rng = np.random.default_rng(seed + 100)
+    if N_seg_end is not None:
+        wl.seg_end = N_seg_end
+    if sigma is not None:
+        wl.seg_sigma = sigma
+    parts, start = [], 0
+    for e, sg in zip(wl.seg_end, wl.seg_sigma):
+        parts.append(rng.standard_normal((e - start, wl.K)).astype(np.float32) * np.float32(sg))
+        start = e
+    wl.data["w32"] = np.concatenate(parts)
+    wl.N = wl.seg_end[-1]
+    return wl
+
+
+@pytest.mark.parametrize("use_linear", [False, True])
+def test_gemm_tiny_config(nv, use_linear):
+    wl = W.generate("tiny_linear_64x128x256")
+    r = _run_layer(nv, wl, use_linear)
+    yref, _, bound = _oracle_side(wl, r)
+    P.assert_within_tolerance(P.y_to_f64(r["y"]), yref, bound, "tiny")
+
+
+@pytest.mark.parametrize("use_linear", [False, True])
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_gemm_decode_config_full(nv, use_linear, mode):
+    wl = W.generate("decode_gemv_4x16384x5120")
+    act = 0.0415 if mode == "static" else None
+    r = _run_layer(nv, wl, use_linear, act_static=act)
+    cols = np.sort(np.random.default_rng(1).choice(wl.N, 2048, replace=False))
+    yref, _, bound = _oracle_side(wl, r, act_static=act, cols=cols)
+    P.assert_within_tolerance(P.y_to_f64(r["y"])[:, cols], yref, bound, "decode")
+
+
+def test_gemm_gdn_in_proj_segments(nv):
+    wl = W.generate("gdn_in_proj_8192x16384x5120", M=267, with_weight=False)
+    _shrink(wl, [256, 512, 1280, 2048])
+    r = _run_layer(nv, wl, use_linear=True, act_static=0.04)
+    yref, _, bound = _oracle_side(wl, r, act_static=0.04)
+    P.assert_within_tolerance(P.y_to_f64(r["y"]), yref, bound, "gdn_in_proj")
+
+
+def test_gemm_gates_epilogue(nv):
+    wl = W.generate("gdn_gates_32768x96x5120", M=300)
+    r = _run_layer(nv, wl, use_linear=True)
+    yref, _, bound = _oracle_side(wl, r)
+    y = P.y_to_f64(r["y"])
+    P.assert_within_tolerance(y, yref, bound, "gates")
+    assert np.all(y[:, :48] < 0) and np.all((y[:, 48:] >= 0) & (y[:, 48:] <= 1))
+
+
+def test_gemm_mlp_gate_up_scales_4x_apart(nv):
+    wl = W.generate("mlp_gate_up_32768x34816x5120", M=150, with_weight=False)
+    _shrink(wl, [512, 1024])
+    g0 = O.global_scale(O.tensor_amax(wl.data["w32"][:512].astype(np.float64)))
+    seg_g = [float(g0), float(np.float32(4) * g0)]
+    r = _run_layer(nv, wl, use_linear=True, seg_gscale=seg_g)
+    yref, _, bound = _oracle_side(wl, r, seg_gscale=seg_g)
+    P.assert_within_tolerance(P.y_to_f64(r["y"]), yref, bound, "mlp")
+
+
+@pytest.mark.parametrize("M", [1, 3, 17])
+@pytest.mark.parametrize("N,seg_end", [(48, [48]), (96, [48, 96]), (130, [2, 130])])
+@pytest.mark.parametrize("K", [16, 48, 272, 640])
+def test_gemm_ragged_shapes(nv, M, N, seg_end, K):
+    rng = np.random.default_rng(M * 1000 + N * 10 + K)
+    x = (rng.standard_normal((M, K)) * 2).astype(np.float32)
+    x[:, rng.integers(0, K)] *= 40
+    bits = W._to_bf16_bits(x)
+    xv = W.bf16_bits_to_f32(bits)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wl = W.Workload(name="ragged", M=M, N=N, K=K, x_dtype="bf16", y_dtype="bf16", seg_end=seg_end,
+                    seg_sigma=[0.02] * len(seg_end), n_hot=1, hot_gain=(40, 40))
+    wl.data.update(x32=x, x_bf16=bits, w32=w)
+    for use_linear in (False, True):
+        r = _run_layer(nv, wl, use_linear)
+        yref, _, bound = _oracle_side(wl, r)
+        P.assert_within_tolerance(P.y_to_f64(r["y"]), yref, bound, f"ragged M={M} N={N} K={K} linear={use_linear}")
+
+
+def test_gemm_deterministic(nv):
+    wl = W.generate("gdn_in_proj_8192x16384x5120", M=200, with_weight=False)
+    _shrink(wl, [256, 512, 1280, 2048])
+    r1 = _run_layer(nv, wl, use_linear=False)
+    r2 = _run_layer(nv, wl, use_linear=False)
+    assert torch.equal(r1["y"], r2["y"])
+
+
+def test_linear_codes_equal_two_stage(nv):
+    """The fused decode path writes the same activation codes as the stand-alone quantizer."""
+    wl = W.generate("decode_gemv_4x16384x5120")
+    r1 = _run_layer(nv, wl, use_linear=True)
+    r2 = _run_layer(nv, wl, use_linear=False)
+    assert np.array_equal(r1["ac"], r2["ac"]) and np.array_equal(r1["as_"], r2["as_"]) and r1["ag"] == r2["ag"]
+    y1, y2 = P.y_to_f64(r1["y"]), P.y_to_f64(r2["y"])
+    assert np.linalg.norm(y1 - y2) / np.linalg.norm(y2) < 1e-3
