@@ -1,0 +1,260 @@
+"""Benchmark of the NVFP4 W4A4 linear layer on one MI355X.
+
+Headline (value): TFLOP/s of the prefill fused GDN input projection
+M=8192, N=16384 (4 segments: q,k 2048; v,z 6144), K=5120, bf16 in/out, including
+the activation quantization (calibrated activation global scale).  One step =
+nvfp4_quantize_act + nvfp4_w4a4_gemm (quantize, block-scaled GEMM, per-segment
+epilogue).  Also reported: the same with dynamic activation scaling (amax pass
+included), the decode GEMV (M=4, N=16384, K=5120) in GB/s of packed weight
+traffic with weight copies rotated past the 256 MB infinity cache, and the CPU
+oracle's throughput on a bounded row sample of the headline workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--all]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A4 NVFP4 GEMM TFLOPS incl. act-quant (M=8192,K=5120); decode GB/s"
+PEAK_MFMA_F16_TFLOPS = 2500.0          # MI355X dense f16/bf16 MFMA
+PEAK_HBM_GBPS = 8000.0                 # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gdn_in_proj_traffic.json")
+KERNEL_SOURCES = ["nvfp4_w4a4_quantized_amd/csrc/gemm.hip", "nvfp4_w4a4_quantized_amd/csrc/nvfp4_device.hpp",
+                  "nvfp4_w4a4_quantized_amd/csrc/launch.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_if_current():
+    """HBM bytes per GEMM launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def setup_layer(nv, wl, seg_gscale=None):
+    import torch
+    from synth import workloads as W
+    xt = dev_bf16(wl.data["x_bf16"]) if wl.x_dtype == "bf16" else torch.from_numpy(wl.data["x32"]).cuda()
+    wt = torch.from_numpy(wl.data["w32"]).cuda()
+    wc, ws = nv.empty_packed(wl.N, wl.K, "cuda")
+    wg = torch.empty(len(wl.seg_end), dtype=torch.float32, device="cuda")
+    nv.nvfp4_pack_weight(wt, wl.seg_end, seg_gscale, wc, ws, wg)
+    torch.cuda.synchronize()
+    del wt
+    return xt, wc, ws, wg
+
+
+def time_prefill(nv, xt, wc, ws, wg, seg_end, steps, warmup, static_g, y_dtype):
+    """Time `steps` steps of quantize + GEMM.  Returns wall ms/step and the mean
+    HIP-event durations of the quantize (and amax) part and of the GEMM launch."""
+    import torch
+    M, K = xt.shape
+    N = wc.shape[0]
+    ac, as_ = nv.empty_packed(M, K, "cuda")
+    gout = torch.empty(1, dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=y_dtype, device="cuda")
+    gin = static_g
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        nv.nvfp4_quantize_act(xt, gin, ac, as_, gout, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        nv.nvfp4_w4a4_gemm(ac, as_, gout, wc, ws, seg_end, wg, y, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    return wall, q_ms, g_ms, y
+
+
+def time_decode(nv, steps, warmup):
+    """Fused decode GEMV (M=4) with weight copies rotated so that the working set
+    exceeds twice the 256 MB infinity cache."""
+    import torch
+    from synth import workloads as W
+    wl = W.generate("decode_gemv_4x16384x5120")
+    xt, wc, ws, wg = setup_layer(nv, wl)
+    n_sets = 12                                   # 12 x 47.2 MB = 566 MB of packed weight
+    copies = [(wc.clone(), ws.clone()) for _ in range(n_sets)]
+    y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device="cuda")
+    gout = torch.empty(1, dtype=torch.float32, device="cuda")
+    gstat = torch.empty(1, dtype=torch.float32, device="cuda")
+    ac, as_ = nv.empty_packed(wl.M, wl.K, "cuda")
+    nv.nvfp4_quantize_act(xt, None, ac, as_, gstat)           # calibrated scale = this tensor's
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        c, s = copies[i % n_sets]
+        nv.nvfp4_w4a4_linear(xt, gstat, gout, c, s, wl.seg_end, wg, y, stream=stream)
+    n = max(steps, 50)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        c, s = copies[i % n_sets]
+        evs[i][0].record(stream)
+        nv.nvfp4_w4a4_linear(xt, gstat, gout, c, s, wl.seg_end, wg, y, stream=stream)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    w_bytes = wl.N * wl.K // 2 + wl.N * wl.K // 16
+    alg_bytes = w_bytes + wl.M * wl.K * 2 + wl.M * wl.N * 2
+    med = float(np.median(ms))
+    return dict(workload=wl.name, ms_median=med, ms_p10=float(np.percentile(ms, 10)),
+                ms_p90=float(np.percentile(ms, 90)), algorithmic_bytes=alg_bytes,
+                gbps=alg_bytes / (med * 1e-3) / 1e9, frac_hbm=alg_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                rotated_weight_sets=n_sets, act_scale="static")
+
+
+def cpu_baseline(wl, static_g, target_s=10.0):
+    """The oracle as it stands, timed on the host on a bounded row sample of the
+    headline workload: quantize the sampled rows of X, dequantize-then-GEMM in
+    float64, round to bf16.  Weight packing by the oracle is done once, untimed."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import nvfp4 as O
+    from synth import workloads as W
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        wc, ws, wg = O.pack_weight(wl.data["w32"].astype(np.float64), wl.seg_end)
+        pack_s = time.perf_counter() - t0
+        x = W.x_values_f32(wl)
+
+        def run(rows):
+            t = time.perf_counter()
+            ac, as_, ag = O.quantize_activation(x[:rows].astype(np.float64), static_g)
+            O.linear_reference(ac, as_, ag, wc, ws, wl.seg_end, wg, "bf16")
+            return time.perf_counter() - t
+
+        rows, t = 64, run(64)
+        while t < target_s and rows < wl.M:           # grow the sample until it takes >= target_s
+            rows = min(wl.M, rows * 2)
+            t = run(rows)
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    flops = 2.0 * rows * wl.N * wl.K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(min(cores, used)), "kind": "oracle",
+            "sample": f"{rows} of {wl.M} rows of the GDN in_proj workload (N={wl.N}, K={wl.K}): oracle "
+                      f"quantize + float64 dequantize-GEMM + bf16 rounding, {t:.1f} s; oracle weight "
+                      f"packing ({pack_s:.1f} s) untimed"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-dynamic", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this layer is benchmarked on a single MI355X; "
+              "--gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nvfp4_w4a4_quantized_amd as nv
+    from synth import workloads as W
+
+    torch.cuda.set_device(0)
+    log("generating the GDN in_proj workload (8192 x 16384 x 5120)")
+    wl = W.generate("gdn_in_proj_8192x16384x5120")
+    xt, wc, ws, wg = setup_layer(nv, wl)
+    M, N, K = wl.M, wl.N, wl.K
+    # calibrated activation scale: this tensor's own amax-derived scale, computed once
+    gstat = torch.empty(1, dtype=torch.float32, device="cuda")
+    ac, as_ = nv.empty_packed(M, K, "cuda")
+    nv.nvfp4_quantize_act(xt, None, ac, as_, gstat)
+    torch.cuda.synchronize()
+    del ac, as_
+    flops = 2.0 * M * N * K
+
+    log("timing prefill (static activation scale)")
+    wall, q_ms, g_ms, _ = time_prefill(nv, xt, wc, ws, wg, wl.seg_end, args.steps, args.warmup, gstat,
+                                       torch.bfloat16)
+    value = flops / (wall * 1e-3) / 1e12
+    gemm_tflops = flops / (g_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "gdn_in_proj_8192x16384x5120", "M": M, "N": N, "K": K,
+                   "segments": wl.seg_end, "act_scale": "static", "x_dtype": "bf16", "y_dtype": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_MFMA_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_MFMA_F16_TFLOPS, 4),
+                     "traffic": traffic_if_current(), "kernel": "k_gemm_tiled",
+                     "kernel_ms": round(g_ms, 4)},
+        "breakdown_ms": {"quantize_act": round(q_ms, 4), "gemm": round(g_ms, 4)},
+    }
+    if not args.no_dynamic:
+        log("timing prefill (dynamic activation scale)")
+        wall_d, qd_ms, gd_ms, _ = time_prefill(nv, xt, wc, ws, wg, wl.seg_end, args.steps, args.warmup, None,
+                                               torch.bfloat16)
+        out["dynamic_act_scale"] = {"value": round(flops / (wall_d * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                                    "ms_per_step": round(wall_d, 4), "amax_and_quantize_ms": round(qd_ms, 4)}
+    del xt, wc, ws
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        log("timing decode GEMV (4 x 16384 x 5120)")
+        out["decode"] = time_decode(nv, args.steps, args.warmup)
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(wl, np.float32(gstat.item()))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
