@@ -235,7 +235,7 @@ def main():
                    "segments": wl.seg_end, "act_scale": "static", "x_dtype": "bf16", "y_dtype": "bf16"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_MFMA_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_MFMA_F16_TFLOPS, 4),
-                     "traffic": traffic_if_current(), "kernel": "k_gemm_tiled",
+                     "traffic": traffic_if_current(), "kernel": "k_gemm_big (256x256 tile, bf16 out)",
                      "kernel_ms": round(g_ms, 4)},
         "breakdown_ms": {"quantize_act": round(q_ms, 4), "gemm": round(g_ms, 4)},
     }

@@ -33,10 +33,20 @@ __device__ __forceinline__ float softplus_f32(float z) {
 
 __device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + expf(-z)); }
 
-// Epilogue for one output element: alpha scaling, optional gate, store.
+// Output kinds of the epilogue (a template parameter, so that every accumulator
+// index stays a compile-time constant).
+enum : int { EPI_F32 = 0, EPI_BF16 = 1, EPI_GATE = 2 };
+
+template <int EPI>
+__device__ __forceinline__ float col_alpha(const GemmArgs& a, int64_t n, float ga) {
+  return ga * a.w_seg_gscale[seg_of_col(a.seg, n)];
+}
+
+// Epilogue for one output element: alpha scaling, optional gate (Eq. 1), store.
+template <int EPI>
 __device__ __forceinline__ void store_out(const GemmArgs& a, int64_t m, int64_t n, float acc, float alpha) {
   float v = acc * alpha;
-  if (a.gate.n_heads > 0) {
+  if constexpr (EPI == EPI_GATE) {
     const int64_t H = a.gate.n_heads;
     if (n < H) {
       const float z = v + a.gate.dt_bias[n];
@@ -45,7 +55,7 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int64_t m, int64_t 
       v = sigmoid_f32(v);
     }
   }
-  if (a.y_type == OutType::BF16) {
+  if constexpr (EPI == EPI_BF16) {
     reinterpret_cast<uint16_t*>(a.y)[m * a.ldy + n] = (uint16_t)f32_to_bf16_bits(v);
   } else {
     reinterpret_cast<float*>(a.y)[m * a.ldy + n] = v;
@@ -103,7 +113,7 @@ __device__ __forceinline__ uint32_t load_scales4(const uint8_t* base, int64_t ro
   }
 }
 
-template <bool ALIGNED>
+template <bool ALIGNED, int EPI>
 __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
   __shared__ u32x4 lds_ca[2][TBM];
   __shared__ u32x4 lds_cw[2][TBN];
@@ -196,14 +206,14 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int64_t n = n0 + wn * 64 + j * 32 + li;
-    if (n >= a.N) continue;
-    const float alpha = ga * a.w_seg_gscale[seg_of_col(a.seg, n)];
+    const bool n_ok = n < a.N;
+    const float alpha = n_ok ? col_alpha<EPI>(a, n, ga) : 0.0f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < a.M) store_out(a, m, n, acc[i][j][r], alpha);
+        if (n_ok && m < a.M) store_out<EPI>(a, m, n, acc[i][j][r], alpha);
       }
   }
 }
@@ -350,22 +360,176 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemv_fused(GemvArgs p) {
         const int64_t n = (int64_t)blockIdx.x * GV_ROWS + sub * 16 + 4 * q + r;
         if (n < N) {
           const float alpha = ga * a.w_seg_gscale[seg_of_col(a.seg, n)];
-          store_out(a, tok, n, acc[r] + o[r], alpha);
+          if (a.gate.n_heads > 0) store_out<EPI_GATE>(a, tok, n, acc[r] + o[r], alpha);
+          else if (a.y_type == OutType::BF16) store_out<EPI_BF16>(a, tok, n, acc[r] + o[r], alpha);
+          else store_out<EPI_F32>(a, tok, n, acc[r] + o[r], alpha);
         }
       }
     }
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Large-tile GEMM for prefill shapes: 256 x 256 output tile per workgroup, BK = 64,
+// 4 waves of 128 x 128 (4 x 4 MFMA 32x32x16 f16, 256 fp32 accumulators per lane).
+// Decode work per wave grows with (128 + 128) while MFMA work grows with 128 x 128,
+// so the per-lane fp4 -> f16 decode stays under the MFMA time.  Packed tiles
+// (codes 16 KiB + scales 2 KiB per K step) are double-buffered in LDS: one barrier
+// per K step; the global loads for step k+2 are in flight while step k computes.
+// Requires K % 64 == 0 (the caller falls back to the 128 x 128 kernel otherwise).
+// ---------------------------------------------------------------------------------
+constexpr int GBM = 256, GBN = 256, GBK = 64;
+
+struct BigRegs {
+  u32x4 ca0, ca1, cw0, cw1;
+  uint32_t sa, sw;
+};
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
+  __shared__ u32x4 lds_ca[2][2][GBM];      // [stage][half][row]
+  __shared__ u32x4 lds_cw[2][2][GBN];
+  __shared__ uint32_t lds_sa[2][GBM];      // [stage][row]
+  __shared__ uint32_t lds_sw[2][GBN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, li = lane & 31;
+
+  const int64_t tiles_m = (a.M + GBM - 1) / GBM;
+  const int64_t tiles_n = (a.N + GBN - 1) / GBN;
+  const int64_t pid = blockIdx.x;
+  const int64_t group = 8;
+  const int64_t per_group = group * tiles_n;
+  const int64_t gid = pid / per_group;
+  const int64_t first_m = gid * group;
+  const int64_t gsize = (tiles_m - first_m) < group ? (tiles_m - first_m) : group;
+  const int64_t bm = first_m + (pid % per_group) % gsize;
+  const int64_t bn = (pid % per_group) / gsize;
+  const int64_t m0 = bm * GBM, n0 = bn * GBN;
+  const int64_t K = a.K;
+  const int64_t kh = K >> 1, kb = K >> 4;
+
+  // loader roles: codes chunk c in {tid, tid + 256}: row = c >> 1, half = c & 1
+  const int lr0 = tid >> 1, lr1 = 128 + (tid >> 1), lh = tid & 1;
+  const bool a_ok0 = m0 + lr0 < a.M, a_ok1 = m0 + lr1 < a.M;
+  const bool w_ok0 = n0 + lr0 < a.N, w_ok1 = n0 + lr1 < a.N;
+  const bool sa_ok = m0 + tid < a.M, sw_ok = n0 + tid < a.N;
+  const uint8_t* pa0 = a.a_codes + (a_ok0 ? m0 + lr0 : 0) * kh + 16 * lh;
+  const uint8_t* pa1 = a.a_codes + (a_ok1 ? m0 + lr1 : 0) * kh + 16 * lh;
+  const uint8_t* pw0 = a.w_codes + (w_ok0 ? n0 + lr0 : 0) * kh + 16 * lh;
+  const uint8_t* pw1 = a.w_codes + (w_ok1 ? n0 + lr1 : 0) * kh + 16 * lh;
+  const uint8_t* psa = a.a_scales + (sa_ok ? m0 + tid : 0) * kb;
+  const uint8_t* psw = a.w_scales + (sw_ok ? n0 + tid : 0) * kb;
+
+  auto gload = [&](int64_t k0) {
+    BigRegs r;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    r.ca0 = a_ok0 ? *reinterpret_cast<const u32x4*>(pa0 + (k0 >> 1)) : z;
+    r.ca1 = a_ok1 ? *reinterpret_cast<const u32x4*>(pa1 + (k0 >> 1)) : z;
+    r.cw0 = w_ok0 ? *reinterpret_cast<const u32x4*>(pw0 + (k0 >> 1)) : z;
+    r.cw1 = w_ok1 ? *reinterpret_cast<const u32x4*>(pw1 + (k0 >> 1)) : z;
+    r.sa = sa_ok ? *reinterpret_cast<const uint32_t*>(psa + (k0 >> 4)) : 0u;
+    r.sw = sw_ok ? *reinterpret_cast<const uint32_t*>(psw + (k0 >> 4)) : 0u;
+    return r;
+  };
+  auto lstore = [&](int st, const BigRegs& r) {
+    lds_ca[st][lh][lr0] = r.ca0;
+    lds_ca[st][lh][lr1] = r.ca1;
+    lds_cw[st][lh][lr0] = r.cw0;
+    lds_cw[st][lh][lr1] = r.cw1;
+    lds_sa[st][tid] = r.sa;
+    lds_sw[st][tid] = r.sw;
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int64_t nk = K / GBK;
+  BigRegs nxt = gload(0);
+  lstore(0, nxt);
+  if (nk > 1) nxt = gload(GBK);
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    __syncthreads();
+    const int st = (int)(kt & 1);
+    if (kt + 1 < nk) lstore(st ^ 1, nxt);
+    if (kt + 2 < nk) nxt = gload((kt + 2) * GBK);
+
+    u32x4 ca[4], cw[4];
+    uint32_t sa[4], sw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + li;
+      ca[i] = lds_ca[st][h][r];
+      sa[i] = lds_sa[st][r] >> (16 * h);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn * 128 + j * 32 + li;
+      cw[j] = lds_cw[st][h][r];
+      sw[j] = lds_sw[st][r] >> (16 * h);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f16x8 A[4], B[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) A[i] = decode8_f16(ca[i][t], scale_f16x2((sa[i] >> (8 * (t >> 1))) & 0xFFu));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) B[j] = decode8_f16(cw[j][t], scale_f16x2((sw[j] >> (8 * (t >> 1))) & 0xFFu));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  const float ga = *a.a_gscale;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + wn * 128 + j * 32 + li;
+    const bool n_ok = n < a.N;
+    const float alpha = n_ok ? col_alpha<EPI>(a, n, ga) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (n_ok && m < a.M) store_out<EPI>(a, m, n, acc[i][j][r], alpha);
+      }
+  }
+}
+
 }  // namespace
 
-hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) {
+template <int EPI>
+static hipError_t launch_gemm_epi(const GemmArgs& a, hipStream_t s) {
+  if (EPI != EPI_GATE && a.K % GBK == 0 && a.M >= 512 && a.N >= 512) {
+    const int64_t big_tiles = ((a.M + GBM - 1) / GBM) * ((a.N + GBN - 1) / GBN);
+    if constexpr (EPI != EPI_GATE) {
+      hipLaunchKernelGGL(k_gemm_big<EPI>, dim3((unsigned)big_tiles), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   const int64_t tiles = ((a.M + TBM - 1) / TBM) * ((a.N + TBN - 1) / TBN);
   if (a.K % 64 == 0)
-    hipLaunchKernelGGL(k_gemm_tiled<true>, dim3((unsigned)tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm_tiled<true, EPI>), dim3((unsigned)tiles), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_gemm_tiled<false>, dim3((unsigned)tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm_tiled<false, EPI>), dim3((unsigned)tiles), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) {
+  if (a.gate.n_heads > 0) return launch_gemm_epi<EPI_GATE>(a, s);
+  if (a.y_type == OutType::BF16) return launch_gemm_epi<EPI_BF16>(a, s);
+  return launch_gemm_epi<EPI_F32>(a, s);
 }
 
 size_t gemv_lds_bytes(int64_t M, int64_t K) { return (size_t)M * (size_t)K * 2; }

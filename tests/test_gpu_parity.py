@@ -294,3 +294,93 @@ def test_linear_codes_equal_two_stage(nv):
     assert np.array_equal(r1["ac"], r2["ac"]) and np.array_equal(r1["as_"], r2["as_"]) and r1["ag"] == r2["ag"]
     y1, y2 = P.y_to_f64(r1["y"]), P.y_to_f64(r2["y"])
     assert np.linalg.norm(y1 - y2) / np.linalg.norm(y2) < 1e-3
+
+
+# ----------------------------------------------------------------------------- large-tile kernel and full sizes
+
+def test_gemm_big_tile_ragged(nv):
+    """M, N >= 512 select the 256 x 256 kernel; ragged edges in both dimensions."""
+    wl = W.generate("gdn_in_proj_8192x16384x5120", M=700, with_weight=False)
+    _shrink(wl, [300, 1000, 1300], sigma=[0.02, 0.05, 0.01])
+    for use_linear in (False, True):
+        r = _run_layer(nv, wl, use_linear, act_static=0.04)
+        yref, _, bound = _oracle_side(wl, r, act_static=0.04)
+        P.assert_within_tolerance(P.y_to_f64(r["y"]), yref, bound, f"big tile linear={use_linear}")
+
+
+def _full_size_check(nv, name, seg_ratio=False, n_rows=24, n_cols=None, seed=5):
+    """Full-size run in bench.py's launch configuration (quantize + GEMM, static
+    activation scale from a dynamic pre-pass); the oracle checks sampled rows
+    (bit-exact activation and weight bytes for them) and the outputs there."""
+    wl = W.generate(name)
+    xv, xt = _x_inputs(wl)
+    w = wl.data["w32"]
+    w64_seg_amax = [O.tensor_amax(w[s0:s1].astype(np.float64))
+                    for s0, s1 in zip([0] + wl.seg_end[:-1], wl.seg_end)]
+    seg_g = None
+    if seg_ratio:
+        g0 = O.global_scale(w64_seg_amax[0])
+        seg_g = [float(np.float32(r) * g0) for r in wl.seg_scale_ratio]
+    wt = P.dev_x(w)
+    wc, ws, wg = P.gpu_pack(nv, wt, wl.seg_end, seg_g)
+    del wt
+    M, N = wl.M, wl.N
+    gstat = torch.empty(1, dtype=torch.float32, device="cuda")
+    ac, as_ = nv.empty_packed(M, wl.K, "cuda")
+    nv.nvfp4_quantize_act(xt, None, ac, as_, gstat)
+    gout = torch.empty(1, dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16 if wl.y_dtype == "bf16" else torch.float32, device="cuda")
+    gate = None
+    if wl.gate_heads:
+        gate = (torch.from_numpy(wl.data["A_log"]).cuda(), torch.from_numpy(wl.data["dt_bias"]).cuda())
+    nv.nvfp4_quantize_act(xt, gstat, ac, as_, gout)
+    nv.nvfp4_w4a4_gemm(ac, as_, gout, wc, ws, wl.seg_end, wg, y, gate=gate)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(M, n_rows, replace=False))
+    rows[-1] = M - 1
+    cols = np.arange(N) if n_cols is None else np.sort(rng.choice(N, n_cols, replace=False))
+    # oracle: global scales from the full tensors, bytes of the sampled rows only
+    ag = O.global_scale(O.tensor_amax(P.x64_of(xv)))
+    assert ag == np.float32(gout.item())
+    if seg_g is None:
+        og = np.array([O.global_scale(a) for a in w64_seg_amax], dtype=np.float32)
+    else:
+        og = np.asarray(seg_g, dtype=np.float32)
+    assert np.array_equal(og, wg.cpu().numpy())
+    oac, oas = O.quantize_rows(P.x64_of(xv[rows]), np.full(len(rows), ag, dtype=np.float32))
+    P.assert_bytes_equal(ac[torch.from_numpy(rows).cuda()].cpu().numpy(), oac, "activation codes (sampled)")
+    P.assert_bytes_equal(as_[torch.from_numpy(rows).cuda()].cpu().numpy(), oas, "activation scales (sampled)")
+    seg = O.segment_rows(wl.seg_end, N)
+    owc, ows = O.quantize_rows(w[cols].astype(np.float64), og[seg[cols]])
+    P.assert_bytes_equal(wc[torch.from_numpy(cols).cuda()].cpu().numpy(), owc, "weight codes (sampled)")
+    P.assert_bytes_equal(ws[torch.from_numpy(cols).cuda()].cpu().numpy(), ows, "weight scales (sampled)")
+    # outputs at the sampled rows x columns
+    gseg = og[seg[cols]]
+    a_hat = O.dequantize_rows(oac, oas, np.full(len(rows), ag, dtype=np.float32))
+    w_hat = O.dequantize_rows(owc, ows, gseg)
+    y64 = a_hat @ w_hat.T
+    absprod = O.gemm_abs_product(oac, oas, owc, ows)
+    alpha = np.float64(ag) * gseg.astype(np.float64)
+    y_gpu = P.y_to_f64(y[torch.from_numpy(rows).cuda()])[:, cols]
+    if gate is None:
+        yref = O.round_output(y64, wl.y_dtype)
+        bound = O.gemm_elem_bound(y64, absprod, alpha, wl.K, wl.y_dtype)
+    else:
+        out64 = O.gate_epilogue_f64(y64, wl.data["A_log"], wl.data["dt_bias"])
+        yref = O.round_output(out64, "f32")
+        bound = O.gate_elem_bound(y64, O.gemm_elem_bound(y64, absprod, alpha, wl.K, "f32"),
+                                  wl.data["A_log"], wl.data["dt_bias"], yref)
+    P.assert_within_tolerance(y_gpu, yref, bound, name)
+
+
+def test_full_gdn_in_proj_sampled(nv):
+    _full_size_check(nv, "gdn_in_proj_8192x16384x5120")
+
+
+def test_full_gdn_gates_sampled(nv):
+    _full_size_check(nv, "gdn_gates_32768x96x5120", n_rows=256)
+
+
+def test_full_mlp_gate_up_sampled(nv):
+    _full_size_check(nv, "mlp_gate_up_32768x34816x5120", seg_ratio=True, n_rows=16, n_cols=4096)
