@@ -17,7 +17,7 @@ SOURCES = ["abi.cpp", "quant.hip", "gemm.hip"]
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-shared",
     "-fvisibility=hidden",

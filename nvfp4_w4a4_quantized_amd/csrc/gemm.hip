@@ -371,12 +371,18 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemv_fused(GemvArgs p) {
 
 // ---------------------------------------------------------------------------------
 // Large-tile GEMM for prefill shapes: 256 x 256 output tile per workgroup, BK = 64,
-// 4 waves of 128 x 128 (4 x 4 MFMA 32x32x16 f16, 256 fp32 accumulators per lane).
-// Decode work per wave grows with (128 + 128) while MFMA work grows with 128 x 128,
-// so the per-lane fp4 -> f16 decode stays under the MFMA time.  Packed tiles
-// (codes 16 KiB + scales 2 KiB per K step) are double-buffered in LDS: one barrier
-// per K step; the global loads for step k+2 are in flight while step k computes.
-// Requires K % 64 == 0 (the caller falls back to the 128 x 128 kernel otherwise).
+// 4 waves of 128 x 128 (4 x 4 MFMA 32x32x16 f16, 256 fp32 accumulators per lane in
+// AGPRs, so one wave per SIMD).  Decode work per wave grows with (128 + 128) while
+// MFMA work grows with 128 x 128.
+//
+// Software pipeline inside a K step (4 MFMA steps of K = 16): while the 16 MFMAs of
+// step t run, the lane decodes the operands of step t+1 (interleaved 1 MFMA : 4 VALU
+// by sched_group_barrier).  During the MFMAs of the last step the wave passes the LDS
+// barrier, reads the next K step's packed codes and decodes its step 0.  Packed tiles
+// (codes 16 KiB + scales 2 KiB per K step) are double-buffered in LDS; the global
+// loads of K step k+2 are issued at the start of step k and only waited for when
+// they are stored to LDS at the start of step k+1.  The LDS barrier waits for LDS
+// traffic only (lgkmcnt), not for those loads.  Requires K % 64 == 0.
 // ---------------------------------------------------------------------------------
 constexpr int GBM = 256, GBN = 256, GBK = 64;
 
@@ -385,11 +391,33 @@ struct BigRegs {
   uint32_t sa, sw;
 };
 
+__device__ __forceinline__ void lds_barrier() {
+  // wait for this wave's LDS reads/writes, then the workgroup barrier
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// E4M3 scale bytes of blocks (2h, 2h+1) -> f16 pair {s0, s1} (exact)
+__device__ __forceinline__ f16x2 scale_pair_f16(uint32_t two_bytes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two_bytes, 1.0f, false);
+}
+
+__device__ __forceinline__ f16x2 bcast(f16x2 p, int hi) {
+  f16x2 r;
+  if (hi) { r[0] = p[1]; r[1] = p[1]; } else { r[0] = p[0]; r[1] = p[0]; }
+  return r;
+}
+
+#define SCHED_MFMA_VALU(n_mfma, n_valu)                          \
+  _Pragma("unroll") for (int _i = 0; _i < (n_mfma); ++_i) {     \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           \
+    __builtin_amdgcn_sched_group_barrier(0x002, (n_valu), 0);    \
+  }
+
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   __shared__ u32x4 lds_ca[2][2][GBM];      // [stage][half][row]
   __shared__ u32x4 lds_cw[2][2][GBN];
-  __shared__ uint32_t lds_sa[2][GBM];      // [stage][row]
+  __shared__ uint32_t lds_sa[2][GBM];      // [stage][row]: 4 scale bytes
   __shared__ uint32_t lds_sw[2][GBN];
 
   const int tid = threadIdx.x;
@@ -444,6 +472,30 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
     lds_sw[st][tid] = r.sw;
   };
 
+  u32x4 ca[4], cw[4];          // packed codes of this lane's rows for the current K step
+  f16x2 pa[4], pw[4];          // scale pairs {block 2h, block 2h+1}
+  auto lread = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + li;
+      ca[i] = lds_ca[st][h][r];
+      pa[i] = scale_pair_f16(reinterpret_cast<const uint16_t*>(&lds_sa[st][r])[h]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn * 128 + j * 32 + li;
+      cw[j] = lds_cw[st][h][r];
+      pw[j] = scale_pair_f16(reinterpret_cast<const uint16_t*>(&lds_sw[st][r])[h]);
+    }
+  };
+  f16x8 A0[4], B0[4], A1[4], B1[4];
+  auto decode = [&](int t, f16x8 A[4], f16x8 B[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[i] = decode8_f16(ca[i][t], bcast(pa[i], t >> 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) B[j] = decode8_f16(cw[j][t], bcast(pw[j], t >> 1));
+  };
+
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -452,44 +504,73 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  auto mfma_step = [&](const f16x8 A[4], const f16x8 B[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
+  };
+
+  // One K step.  STORE: write the prefetched tile k+1 to the other LDS stage;
+  // LOAD: issue the global loads of tile k+2; NEXT: pass the barrier and read tile
+  // k+1 from LDS during the last MFMA step.
   const int64_t nk = K / GBK;
-  BigRegs nxt = gload(0);
+  BigRegs nxt;
+  auto kstep = [&]<bool STORE, bool LOAD, bool NEXT>(int64_t kt) {
+    const int st = (int)(kt & 1);
+    // step 0 MFMAs | decode step 1, LDS store of tile k+1, global loads of tile k+2
+    mfma_step(A0, B0);
+    decode(1, A1, B1);
+    if constexpr (STORE) lstore(st ^ 1, nxt);
+    if constexpr (LOAD) nxt = gload((kt + 2) * GBK);
+    if constexpr (STORE && LOAD) {
+#pragma unroll
+      for (int q = 0; q < 6; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      SCHED_MFMA_VALU(10, 4)
+    } else {
+      SCHED_MFMA_VALU(16, 4)
+    }
+    // step 1 MFMAs | decode step 2
+    mfma_step(A1, B1);
+    decode(2, A0, B0);
+    SCHED_MFMA_VALU(16, 4)
+    // step 2 MFMAs | decode step 3
+    mfma_step(A0, B0);
+    decode(3, A1, B1);
+    SCHED_MFMA_VALU(16, 4)
+    if constexpr (NEXT) {
+      // tile k+1 is complete in LDS once every wave has passed here
+      lds_barrier();
+      lread(st ^ 1);
+      mfma_step(A1, B1);
+      decode(0, A0, B0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      SCHED_MFMA_VALU(12, 6)
+    } else {
+      mfma_step(A1, B1);
+    }
+  };
+
+  nxt = gload(0);
   lstore(0, nxt);
   if (nk > 1) nxt = gload(GBK);
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    __syncthreads();
-    const int st = (int)(kt & 1);
-    if (kt + 1 < nk) lstore(st ^ 1, nxt);
-    if (kt + 2 < nk) nxt = gload((kt + 2) * GBK);
-
-    u32x4 ca[4], cw[4];
-    uint32_t sa[4], sw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 128 + i * 32 + li;
-      ca[i] = lds_ca[st][h][r];
-      sa[i] = lds_sa[st][r] >> (16 * h);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn * 128 + j * 32 + li;
-      cw[j] = lds_cw[st][h][r];
-      sw[j] = lds_sw[st][r] >> (16 * h);
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f16x8 A[4], B[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) A[i] = decode8_f16(ca[i][t], scale_f16x2((sa[i] >> (8 * (t >> 1))) & 0xFFu));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) B[j] = decode8_f16(cw[j][t], scale_f16x2((sw[j] >> (8 * (t >> 1))) & 0xFFu));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
-    }
-  }
+  lds_barrier();
+  lread(0);
+  decode(0, A0, B0);
+  int64_t kt = 0;
+  for (; kt + 2 < nk; ++kt) kstep.template operator()<true, true, true>(kt);
+  if (kt + 1 < nk) { kstep.template operator()<true, false, true>(kt); ++kt; }
+  kstep.template operator()<false, false, false>(kt);
 
   const float ga = *a.a_gscale;
 #pragma unroll
