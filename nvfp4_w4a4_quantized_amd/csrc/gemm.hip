@@ -375,25 +375,31 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemv_fused(GemvArgs p) {
 // AGPRs, so one wave per SIMD).  Decode work per wave grows with (128 + 128) while
 // MFMA work grows with 128 x 128.
 //
+// Data movement: packed tiles (codes 16 KiB + scales 2 KiB per K step) go from HBM
+// straight into a 4-stage LDS ring with gfx950's direct-to-LDS loads (no staging
+// registers, no ds_write); the loads of K step k+3 are issued while step k computes.
+// Before the barrier that publishes stage k+1 each wave waits only for its own loads
+// of that stage (vmcnt), so two later stages stay in flight.
+//
 // Software pipeline inside a K step (4 MFMA steps of K = 16): while the 16 MFMAs of
 // step t run, the lane decodes the operands of step t+1 (interleaved 1 MFMA : 4 VALU
-// by sched_group_barrier).  During the MFMAs of the last step the wave passes the LDS
-// barrier, reads the next K step's packed codes and decodes its step 0.  Packed tiles
-// (codes 16 KiB + scales 2 KiB per K step) are double-buffered in LDS; the global
-// loads of K step k+2 are issued at the start of step k and only waited for when
-// they are stored to LDS at the start of step k+1.  The LDS barrier waits for LDS
-// traffic only (lgkmcnt), not for those loads.  Requires K % 64 == 0.
+// by sched_group_barrier).  The barrier sits before the last MFMA step, so the next
+// K step's LDS reads and its step-0 decode run under those MFMAs.
+// Requires K % 64 == 0 and K >= 192 (three K steps).
 // ---------------------------------------------------------------------------------
 constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int GST = 4;                                  // LDS stages
+constexpr int ST_A = 0, ST_W = 8192, ST_SA = 16384, ST_SW = 17408, ST_BYTES = 18432;
 
-struct BigRegs {
-  u32x4 ca0, ca1, cw0, cw1;
-  uint32_t sa, sw;
-};
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("s_barrier" ::: "memory");
+}
 
-__device__ __forceinline__ void lds_barrier() {
-  // wait for this wave's LDS reads/writes, then the workgroup barrier
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt not waited for)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // E4M3 scale bytes of blocks (2h, 2h+1) -> f16 pair {s0, s1} (exact)
@@ -415,10 +421,7 @@ __device__ __forceinline__ f16x2 bcast(f16x2 p, int hi) {
 
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
-  __shared__ u32x4 lds_ca[2][2][GBM];      // [stage][half][row]
-  __shared__ u32x4 lds_cw[2][2][GBN];
-  __shared__ uint32_t lds_sa[2][GBM];      // [stage][row]: 4 scale bytes
-  __shared__ uint32_t lds_sw[2][GBN];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[GST * ST_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -440,52 +443,56 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   const int64_t K = a.K;
   const int64_t kh = K >> 1, kb = K >> 4;
 
-  // loader roles: codes chunk c in {tid, tid + 256}: row = c >> 1, half = c & 1
-  const int lr0 = tid >> 1, lr1 = 128 + (tid >> 1), lh = tid & 1;
-  const bool a_ok0 = m0 + lr0 < a.M, a_ok1 = m0 + lr1 < a.M;
-  const bool w_ok0 = n0 + lr0 < a.N, w_ok1 = n0 + lr1 < a.N;
-  const bool sa_ok = m0 + tid < a.M, sw_ok = n0 + tid < a.N;
-  const uint8_t* pa0 = a.a_codes + (a_ok0 ? m0 + lr0 : 0) * kh + 16 * lh;
-  const uint8_t* pa1 = a.a_codes + (a_ok1 ? m0 + lr1 : 0) * kh + 16 * lh;
-  const uint8_t* pw0 = a.w_codes + (w_ok0 ? n0 + lr0 : 0) * kh + 16 * lh;
-  const uint8_t* pw1 = a.w_codes + (w_ok1 ? n0 + lr1 : 0) * kh + 16 * lh;
-  const uint8_t* psa = a.a_scales + (sa_ok ? m0 + tid : 0) * kb;
-  const uint8_t* psw = a.w_scales + (sw_ok ? n0 + tid : 0) * kb;
-
-  auto gload = [&](int64_t k0) {
-    BigRegs r;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    r.ca0 = a_ok0 ? *reinterpret_cast<const u32x4*>(pa0 + (k0 >> 1)) : z;
-    r.ca1 = a_ok1 ? *reinterpret_cast<const u32x4*>(pa1 + (k0 >> 1)) : z;
-    r.cw0 = w_ok0 ? *reinterpret_cast<const u32x4*>(pw0 + (k0 >> 1)) : z;
-    r.cw1 = w_ok1 ? *reinterpret_cast<const u32x4*>(pw1 + (k0 >> 1)) : z;
-    r.sa = sa_ok ? *reinterpret_cast<const uint32_t*>(psa + (k0 >> 4)) : 0u;
-    r.sw = sw_ok ? *reinterpret_cast<const uint32_t*>(psw + (k0 >> 4)) : 0u;
-    return r;
-  };
-  auto lstore = [&](int st, const BigRegs& r) {
-    lds_ca[st][lh][lr0] = r.ca0;
-    lds_ca[st][lh][lr1] = r.ca1;
-    lds_cw[st][lh][lr0] = r.cw0;
-    lds_cw[st][lh][lr1] = r.cw1;
-    lds_sa[st][tid] = r.sa;
-    lds_sw[st][tid] = r.sw;
+  // LDS stage layout: codes [row][32 B] (both halves of the row's 64 elements), the
+  // two 16-byte halves of row r stored in swapped order when bit 2 xor bit 3 of r is
+  // set, which makes the per-lane 16-byte reads below conflict-free; scales [row][4 B].
+  // Load roles (per wave, per K step): 2 x 32 rows of A codes and of W codes (lanes
+  // 2j and 2j+1 fetch the two halves of one row: 32 contiguous bytes), 64 rows of A
+  // and of W scales.  Rows past M or N are clamped to the last row (in bounds; their
+  // outputs are never stored).
+  const uint8_t* ga_c[2];
+  const uint8_t* gw_c[2];
+  uint32_t lo_c[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r0 = 32 * (2 * wave + q);
+    const int row = r0 + (lane >> 1);
+    const int hl = (lane & 1) ^ (((row >> 2) ^ (row >> 3)) & 1);      // logical half of this slot
+    const int64_t ra = min<int64_t>(m0 + row, a.M - 1);
+    const int64_t rw = min<int64_t>(n0 + row, a.N - 1);
+    ga_c[q] = a.a_codes + ra * kh + 16 * hl;
+    gw_c[q] = a.w_codes + rw * kh + 16 * hl;
+    lo_c[q] = (uint32_t)(r0 * 32);
+  }
+  const uint8_t* ga_s = a.a_scales + min<int64_t>(m0 + 64 * wave + lane, a.M - 1) * kb;
+  const uint8_t* gw_s = a.w_scales + min<int64_t>(n0 + 64 * wave + lane, a.N - 1) * kb;
+  const uint32_t lo_s = (uint32_t)(64 * wave * 4);
+  auto issue = [&](int st, int64_t k0) {
+    uint8_t* base = smem + st * ST_BYTES;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      __builtin_amdgcn_global_load_lds(ga_c[q] + (k0 >> 1), base + ST_A + lo_c[q], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(gw_c[q] + (k0 >> 1), base + ST_W + lo_c[q], 16, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds(ga_s + (k0 >> 4), base + ST_SA + lo_s, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(gw_s + (k0 >> 4), base + ST_SW + lo_s, 4, 0, 0);
   };
 
   u32x4 ca[4], cw[4];          // packed codes of this lane's rows for the current K step
   f16x2 pa[4], pw[4];          // scale pairs {block 2h, block 2h+1}
   auto lread = [&](int st) {
+    const uint8_t* base = smem + st * ST_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 128 + i * 32 + li;
-      ca[i] = lds_ca[st][h][r];
-      pa[i] = scale_pair_f16(reinterpret_cast<const uint16_t*>(&lds_sa[st][r])[h]);
+      ca[i] = *reinterpret_cast<const u32x4*>(base + ST_A + r * 32 + 16 * (h ^ (((r >> 2) ^ (r >> 3)) & 1)));
+      pa[i] = scale_pair_f16(*reinterpret_cast<const uint16_t*>(base + ST_SA + r * 4 + 2 * h));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = wn * 128 + j * 32 + li;
-      cw[j] = lds_cw[st][h][r];
-      pw[j] = scale_pair_f16(reinterpret_cast<const uint16_t*>(&lds_sw[st][r])[h]);
+      cw[j] = *reinterpret_cast<const u32x4*>(base + ST_W + r * 32 + 16 * (h ^ (((r >> 2) ^ (r >> 3)) & 1)));
+      pw[j] = scale_pair_f16(*reinterpret_cast<const uint16_t*>(base + ST_SW + r * 4 + 2 * h));
     }
   };
   f16x8 A0[4], B0[4], A1[4], B1[4];
@@ -512,24 +519,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
   };
 
-  // One K step.  STORE: write the prefetched tile k+1 to the other LDS stage;
-  // LOAD: issue the global loads of tile k+2; NEXT: pass the barrier and read tile
-  // k+1 from LDS during the last MFMA step.
+  // One K step.  LOAD: issue the loads of tile k+3; NEXT: publish and read tile k+1
+  // during the last MFMA step; VM: loads allowed in flight when tile k+1 is needed.
   const int64_t nk = K / GBK;
-  BigRegs nxt;
-  auto kstep = [&]<bool STORE, bool LOAD, bool NEXT>(int64_t kt) {
-    const int st = (int)(kt & 1);
-    // step 0 MFMAs | decode step 1, LDS store of tile k+1, global loads of tile k+2
+  auto kstep = [&]<bool LOAD, bool NEXT, int VM>(int64_t kt) {
+    // step 0 MFMAs | decode step 1, loads of tile k+3
     mfma_step(A0, B0);
     decode(1, A1, B1);
-    if constexpr (STORE) lstore(st ^ 1, nxt);
-    if constexpr (LOAD) nxt = gload((kt + 2) * GBK);
-    if constexpr (STORE && LOAD) {
+    if constexpr (LOAD) {
+      issue((int)((kt + 3) & 3), (kt + 3) * GBK);
 #pragma unroll
       for (int q = 0; q < 6; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       SCHED_MFMA_VALU(10, 4)
@@ -545,9 +547,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
     decode(3, A1, B1);
     SCHED_MFMA_VALU(16, 4)
     if constexpr (NEXT) {
-      // tile k+1 is complete in LDS once every wave has passed here
-      lds_barrier();
-      lread(st ^ 1);
+      wait_vmcnt<VM>();                 // this wave's loads of tile k+1 have landed
+      wg_barrier();                     // ... and every other wave's
+      lread((int)((kt + 1) & 3));
       mfma_step(A1, B1);
       decode(0, A0, B0);
 #pragma unroll
@@ -561,16 +563,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
     }
   };
 
-  nxt = gload(0);
-  lstore(0, nxt);
-  if (nk > 1) nxt = gload(GBK);
-  lds_barrier();
+  issue(0, 0);
+  issue(1, GBK);
+  issue(2, 2 * GBK);
+  wait_vmcnt<12>();
+  wg_barrier();
   lread(0);
   decode(0, A0, B0);
   int64_t kt = 0;
-  for (; kt + 2 < nk; ++kt) kstep.template operator()<true, true, true>(kt);
-  if (kt + 1 < nk) { kstep.template operator()<true, false, true>(kt); ++kt; }
-  kstep.template operator()<false, false, false>(kt);
+  for (; kt + 3 < nk; ++kt) kstep.template operator()<true, true, 12>(kt);
+  kstep.template operator()<false, true, 6>(kt);       // kt = nk - 3
+  ++kt;
+  kstep.template operator()<false, true, 0>(kt);       // kt = nk - 2
+  ++kt;
+  kstep.template operator()<false, false, 0>(kt);      // kt = nk - 1
 
   const float ga = *a.a_gscale;
 #pragma unroll
@@ -592,7 +598,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
 
 template <int EPI>
 static hipError_t launch_gemm_epi(const GemmArgs& a, hipStream_t s) {
-  if (EPI != EPI_GATE && a.K % GBK == 0 && a.M >= 512 && a.N >= 512) {
+  if (EPI != EPI_GATE && a.K % GBK == 0 && a.K >= 3 * GBK && a.M >= 512 && a.N >= 512) {
     const int64_t big_tiles = ((a.M + GBM - 1) / GBM) * ((a.N + GBN - 1) / GBN);
     if constexpr (EPI != EPI_GATE) {
       hipLaunchKernelGGL(k_gemm_big<EPI>, dim3((unsigned)big_tiles), dim3(256), 0, s, a);
