@@ -131,23 +131,34 @@ def time_decode(nv, steps, warmup):
     for i in range(warmup):
         c, s = copies[i % n_sets]
         nv.nvfp4_w4a4_linear(xt, gstat, gout, c, s, wl.seg_end, wg, y, stream=stream)
-    n = max(steps, 50)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    # steady state: back-to-back calls on rotated weights, one event pair around them
+    n = max(steps, 120)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    e0.record(stream)
     for i in range(n):
+        c, s = copies[i % n_sets]
+        nv.nvfp4_w4a4_linear(xt, gstat, gout, c, s, wl.seg_end, wg, y, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_call = e0.elapsed_time(e1) / n
+    # single-call latency (an event pair around each call: includes launch overhead)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+    for i in range(50):
         c, s = copies[i % n_sets]
         evs[i][0].record(stream)
         nv.nvfp4_w4a4_linear(xt, gstat, gout, c, s, wl.seg_end, wg, y, stream=stream)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    single = np.array([a.elapsed_time(b) for a, b in evs])
     w_bytes = wl.N * wl.K // 2 + wl.N * wl.K // 16
     alg_bytes = w_bytes + wl.M * wl.K * 2 + wl.M * wl.N * 2
-    med = float(np.median(ms))
-    return dict(workload=wl.name, ms_median=med, ms_p10=float(np.percentile(ms, 10)),
-                ms_p90=float(np.percentile(ms, 90)), algorithmic_bytes=alg_bytes,
-                gbps=alg_bytes / (med * 1e-3) / 1e9, frac_hbm=alg_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                rotated_weight_sets=n_sets, act_scale="static")
+    gbps = alg_bytes / (per_call * 1e-3) / 1e9
+    return dict(workload=wl.name, us_per_call=round(per_call * 1e3, 3), gbps=round(gbps, 1),
+                frac_hbm=round(gbps / PEAK_HBM_GBPS, 4), algorithmic_bytes=alg_bytes,
+                single_call_us_median=round(float(np.median(single)) * 1e3, 3),
+                rotated_weight_sets=n_sets, calls=n, act_scale="static",
+                timing="back-to-back calls, rotated weight copies, one event pair around all calls")
 
 
 def cpu_baseline(wl, static_g, target_s=10.0):
@@ -190,6 +201,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dynamic", action="store_true")
+    ap.add_argument("--decode-only", action="store_true", help="time only the decode GEMV (no JSON contract line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this layer is benchmarked on a single MI355X; "
@@ -201,6 +213,9 @@ def main():
     from synth import workloads as W
 
     torch.cuda.set_device(0)
+    if args.decode_only:
+        print(json.dumps({"decode": time_decode(nv, args.steps, args.warmup)}), flush=True)
+        return
     log("generating the GDN in_proj workload (8192 x 16384 x 5120)")
     wl = W.generate("gdn_in_proj_8192x16384x5120")
     xt, wc, ws, wg = setup_layer(nv, wl)

@@ -176,7 +176,8 @@ hipError_t enqueue_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t 
 constexpr int64_t kGemvMaxM = 8;
 constexpr int64_t kGemvLdsBudget = 56 * 1024;
 
-bool gemv_fits(int64_t M, int64_t K) {
+bool gemv_fits(int64_t M, int64_t K, int32_t x_dtype) {
+  if (nvfp4::gemv_stream_fits(M, K, in_type(x_dtype))) return true;
   return M <= kGemvMaxM && K % 128 == 0 && M * K * 2 <= kGemvLdsBudget;
 }
 
@@ -268,7 +269,7 @@ int32_t nvfp4_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, 
   nvfp4::GemmArgs g{};
   st = check_gemm_common(M, N, K, w_codes, w_scales, n_seg, seg_end, w_seg_gscale, gate, y, y_dtype, ldy, &g);
   if (st) return st;
-  const bool fused_gemv = gemv_fits(M, K);
+  const bool fused_gemv = gemv_fits(M, K, x_dtype);
   if (!fused_gemv && !a_codes_out)
     return fail(NVFP4_ERR_INVALID_ARG,
                 "this shape (M=%lld, N=%lld, K=%lld) runs in two stages and needs a_codes_out/a_scales_out",

@@ -64,5 +64,7 @@ struct GemvArgs {
   GemmArgs g;                  // a_codes/a_scales/a_gscale unused
 };
 hipError_t launch_gemv_fused(const GemvArgs& a, hipStream_t s);
+// Whether the streaming decode GEMV handles this shape (else the LDS-f16 fallback).
+bool gemv_stream_fits(int64_t M, int64_t K, InType t);
 
 }  // namespace nvfp4

@@ -7,16 +7,19 @@
 //
 // Exactness.  The block scale is E4M3-RNE of t = amax_block / (6 g) and each code is
 // E2M1-RNE of |x| / (s g), both of the *exact* quotient.
-//  * Block scale: one float64 division.  A float64 quotient never crosses or lands on
-//    an E4M3 midpoint unless the exact quotient is on it (midpoints have <= 5
-//    significant bits, 6g has <= 27, amax <= 24: a non-zero gap is >= ~2^-32
-//    relative, the division error <= 2^-53), so rounding it is exact.
-//  * Codes: fast path y = x * fp32(1/(s g)) converted by the hardware E2M1 RNE
-//    conversion (v_cvt_scalef32_pk_fp4_f32, exact RNE with saturation at 6 and the
-//    sign of x kept, power-of-two scale 1.0).  |y - r| <= 2 ulp(y); a code can only
-//    be wrong if a midpoint lies within that distance, and every midpoint has its
-//    low 21 mantissa bits zero.  Any y within 8 ulps of such a value is redone
-//    exactly in float64 (mu * s * g is exact there) - rare on real data.
+//  * Block scale: fast path t' = amax * fp32(1/(6g)) in fp32 (|t' - t| <= 2 ulp) rounded
+//    to E4M3 with integer arithmetic.  Every E4M3 midpoint (and every other value with
+//    <= 4 significant bits) has its low 19 mantissa bits zero; a t' within 8 ulps of
+//    such a value is redone exactly: one float64 division, whose result never crosses
+//    or lands on an E4M3 midpoint unless the exact quotient does (midpoints have <= 5
+//    significant bits, 6g <= 27, amax <= 24: a non-zero gap is >= ~2^-32 relative,
+//    the division error <= 2^-53).
+//  * Codes: y = x * rcp(s g) in fp32 (|y - r| <= 3 ulp(y)) converted by the hardware
+//    E2M1 RNE conversion (v_cvt_scalef32_pk_fp4_f32: exact RNE with saturation at 6,
+//    the sign of x kept, power-of-two scale 1.0).  A code can only be wrong if a
+//    midpoint lies within that distance; every midpoint has its low 21 mantissa bits
+//    zero, and any y within 16 ulps of such a value is redone exactly in float64
+//    (mu * s * g is exact there).  Rare on real data.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,8 +45,10 @@ __device__ __forceinline__ float global_scale_from_amax(float amax) {
   return (float)((double)amax / 2688.0);
 }
 
-// Exact E4M3 block-scale byte for block amax a >= 0 under global scale g >= 0.
-__device__ __forceinline__ uint32_t block_scale_byte(float a, float g) {
+// Exact E4M3 block-scale byte for block amax a >= 0 under global scale g >= 0, by
+// float64 division (the reference path).  Inlined on purpose: a call would make the
+// compiler wait for every outstanding memory operation (vmcnt(0)) at the call site.
+__device__ __forceinline__ uint32_t block_scale_byte_exact(float a, float g) {
   if (!(a > 0.0f) || !(g > 0.0f)) return 0u;
   const double t = (double)a / (6.0 * (double)g);
   if (t >= 448.0) return 0x7Eu;                    // saturate at the largest finite value
@@ -58,26 +63,62 @@ __device__ __forceinline__ uint32_t block_scale_byte(float a, float g) {
   return ((uint32_t)(e + 7) << 3) | m3;                      // <= 0x7E because t < 448
 }
 
-// Exact E2M1 code of x under h = s * g (float64, exact product), h > 0.
-__device__ __noinline__ uint32_t e2m1_code_exact(float x, double h) {
+// Per-tensor constants of the fast block-scale path.
+struct ScaleConsts {
+  float g;        // global scale
+  float inv6g;    // fp32(1 / (6 g)), 0 when g == 0
+};
+
+__device__ __forceinline__ ScaleConsts scale_consts(float g) {
+  ScaleConsts c;
+  c.g = g;
+  c.inv6g = (g > 0.0f) ? (float)(1.0 / (6.0 * (double)g)) : 0.0f;
+  return c;
+}
+
+// E4M3 RNE (saturating) of an fp32 t >= 0 with integer arithmetic.
+__device__ __forceinline__ uint32_t e4m3_rne_from_f32(float t) {
+  if (!(t < 448.0f)) return 0x7Eu;
+  if (t < 0x1p-6f) {                                   // subnormal E4M3: multiples of 2^-9
+    return (uint32_t)__builtin_rintf(t * 512.0f);      // exact scaling; RNE; 8 -> 0x08
+  }
+  uint32_t b = __float_as_uint(t);
+  b += 0x7FFFFu + ((b >> 20) & 1u);                    // RNE to 3 mantissa bits
+  return ((((b >> 23) & 0xFFu) - 120u) << 3) | ((b >> 20) & 7u);
+}
+
+// Exact E4M3 block-scale byte (fast path with an exact fallback near midpoints).
+__device__ __forceinline__ uint32_t block_scale_byte(float a, const ScaleConsts& c) {
+  const float t = a * c.inv6g;
+  const uint32_t key = (__float_as_uint(t) + 8u) & 0x7FFFFu;     // near a <= 4-bit value?
+  if (key <= 16u || !(t < 0x1p100f) || (t < 0x1p-100f && t != 0.0f)) return block_scale_byte_exact(a, c.g);
+  if (!(a > 0.0f) || !(c.g > 0.0f)) return 0u;
+  if (t <= 0x1p-10f) return 0u;
+  return e4m3_rne_from_f32(t);
+}
+
+__device__ __forceinline__ uint32_t block_scale_byte(float a, float g) {
+  return block_scale_byte(a, scale_consts(g));
+}
+
+// Exact E2M1 code of x under h = s * g (float64, exact product), h > 0.  Inlined for
+// the same reason as block_scale_byte_exact.
+__device__ __forceinline__ uint32_t e2m1_code_exact(float x, double h) {
   const double a = __builtin_fabs((double)x);
   uint32_t c = (a > 0.25 * h) + (a >= 0.75 * h) + (a > 1.25 * h) + (a >= 1.75 * h) +
                (a > 2.5 * h) + (a >= 3.5 * h) + (a > 5.0 * h);
   return c | ((__float_as_uint(x) >> 28) & 8u);
 }
 
-// Is y (the approximate quotient) within 8 ulps of a value whose low 21 mantissa
-// bits are zero (every E2M1 midpoint is one)?  Returns a value < 17 if so.
-__device__ __forceinline__ uint32_t near_key(float y) {
-  return (__float_as_uint(y) + 8u) & 0x1FFFFFu;
-}
-
 // Quantize the 8 consecutive values v[0..7] of one block (block scale byte sb,
 // global scale g).  Returns the 8 codes packed, element 0 in the low nibble.
 __device__ __forceinline__ uint32_t quant8(const float v[8], uint32_t sb, float g) {
-  const double h = (double)e4m3_to_f32(sb) * (double)g;     // exact
-  float rh = (h > 0.0) ? (float)(1.0 / h) : 0.0f;            // 0 -> codes keep only the sign
-  const bool fast_ok = (h == 0.0) || (h >= 0x1p-120);
+  const float s = e4m3_to_f32(sb);
+  const float h32 = s * g;
+  const bool zero = (sb == 0u) || !(g > 0.0f);
+  // fast path valid while s g and 1/(s g) are normal fp32 values
+  const bool fast_ok = zero || (h32 >= 0x1p-120f && h32 <= 0x1p120f);
+  const float rh = zero ? 0.0f : __builtin_amdgcn_rcpf(h32);   // <= 1 ulp; 0 keeps only the sign
   float y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = v[i] * rh;
@@ -86,10 +127,17 @@ __device__ __forceinline__ uint32_t quant8(const float v[8], uint32_t sb, float 
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
-  uint32_t k = near_key(y[0]);
+  // key(y) = low 21 mantissa bits of y + 16, moved to the top: < 33 << 11 iff y is
+  // within 16 ulps of a value whose low 21 mantissa bits are zero
+  uint32_t k = 0xFFFFFFFFu;
 #pragma unroll
-  for (int i = 1; i < 8; ++i) k = min(k, near_key(y[i]));
-  if (h > 0.0 && (k <= 16u || !fast_ok)) {
+  for (int i = 0; i < 8; i += 2) {
+    const uint32_t k0 = (__float_as_uint(y[i]) << 11) + (16u << 11);
+    const uint32_t k1 = (__float_as_uint(y[i + 1]) << 11) + (16u << 11);
+    k = min(k, min(k0, k1));
+  }
+  if (!zero && (k < (33u << 11) || !fast_ok)) {
+    const double h = (double)s * (double)g;                   // exact
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t c = e2m1_code_exact(v[i], h);

@@ -43,41 +43,59 @@ __device__ __forceinline__ int seg_of(const SegTable& seg, int64_t row) {
   return s;
 }
 
-// Each wave walks "segments" of 64 chunks (512 elements) of one row.
+// Each wave walks "segments" of 64 chunks (512 elements) of one row, QU segments per
+// iteration with all their loads issued before any is used (4 x 16 bytes in flight
+// per lane).  The per-segment scale constants (global scale and fp32(1/(6g))) are
+// computed once per workgroup into LDS.
+constexpr int QU = 4;
+
 template <InType T>
 __global__ __launch_bounds__(kThreads) void k_quant_rows(const void* __restrict__ x, int64_t rows,
                                                          int64_t K, int64_t ld,
                                                          const float* __restrict__ gvec, SegTable seg,
                                                          uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ scales) {
+  __shared__ ScaleConsts sc_lds[kMaxSeg];
+  if ((int)threadIdx.x < seg.n) sc_lds[threadIdx.x] = scale_consts(gvec[threadIdx.x]);
+  __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const uint32_t chunks = (uint32_t)(K >> 3);
   const uint32_t segs_per_row = (chunks + 63u) >> 6;
   const uint64_t total = (uint64_t)rows * segs_per_row;
-  for (uint64_t sgi = (uint64_t)blockIdx.x * kWaves + wave; sgi < total;
-       sgi += (uint64_t)gridDim.x * kWaves) {
-    const uint64_t row = sgi / segs_per_row;
-    const uint32_t chunk = (uint32_t)(sgi - row * segs_per_row) * 64u + lane;
-    const bool valid = chunk < chunks;
-    const int64_t col = (int64_t)chunk * 8;
-    float v[8];
-    if (valid) {
-      load8<T>(x, (int64_t)row * ld + col, v);
-    } else {
+  const uint64_t stride = (uint64_t)gridDim.x * kWaves * QU;
+  for (uint64_t base = ((uint64_t)blockIdx.x * kWaves + wave) * QU; base < total; base += stride) {
+    float v[QU][8];
+    uint64_t row[QU];
+    uint32_t chunk[QU];
+    bool valid[QU];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    for (int u = 0; u < QU; ++u) {
+      const uint64_t sgi = base + u;
+      row[u] = sgi / segs_per_row;
+      chunk[u] = (uint32_t)(sgi - row[u] * segs_per_row) * 64u + lane;
+      valid[u] = sgi < total && chunk[u] < chunks;
+      if (valid[u]) {
+        load8<T>(x, (int64_t)row[u] * ld + (int64_t)chunk[u] * 8, v[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+      }
     }
-    float a = __builtin_fabsf(v[0]);
 #pragma unroll
-    for (int i = 1; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
-    a = __builtin_fmaxf(a, dpp_swap_adjacent(a));
-    const float g = gvec[seg_of(seg, (int64_t)row)];
-    const uint32_t sb = block_scale_byte(a, g);
-    const uint32_t w = quant8(v, sb, g);
-    if (valid) {
-      *reinterpret_cast<uint32_t*>(codes + (int64_t)row * (K >> 1) + (col >> 1)) = w;
-      if ((lane & 1) == 0) scales[(int64_t)row * (K >> 4) + (col >> 4)] = (uint8_t)sb;
+    for (int u = 0; u < QU; ++u) {
+      float a = __builtin_fabsf(v[u][0]);
+#pragma unroll
+      for (int i = 1; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[u][i]));
+      a = __builtin_fmaxf(a, dpp_swap_adjacent(a));
+      const ScaleConsts sc = sc_lds[seg_of(seg, (int64_t)(valid[u] ? row[u] : 0))];
+      const uint32_t sb = block_scale_byte(a, sc);
+      const uint32_t w = quant8(v[u], sb, sc.g);
+      if (valid[u]) {
+        const int64_t col = (int64_t)chunk[u] * 8;
+        *reinterpret_cast<uint32_t*>(codes + (int64_t)row[u] * (K >> 1) + (col >> 1)) = w;
+        if ((lane & 1) == 0) scales[(int64_t)row[u] * (K >> 4) + (col >> 4)] = (uint8_t)sb;
+      }
     }
   }
 }
@@ -164,7 +182,7 @@ hipError_t launch_quant_rows(const void* x, InType t, int64_t rows, int64_t K, i
                              const float* gvec, const SegTable& seg, uint8_t* codes, uint8_t* scales,
                              hipStream_t s) {
   const uint64_t segs = (uint64_t)rows * (uint64_t)((K / 8 + 63) / 64);
-  const int grid = grid_for(segs);
+  const int grid = grid_for((segs + QU - 1) / QU);
   if (t == InType::BF16)
     hipLaunchKernelGGL(k_quant_rows<InType::BF16>, dim3(grid), dim3(kThreads), 0, s, x, rows, K, ld, gvec, seg,
                        codes, scales);

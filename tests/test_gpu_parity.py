@@ -384,3 +384,27 @@ def test_full_gdn_gates_sampled(nv):
 
 def test_full_mlp_gate_up_sampled(nv):
     _full_size_check(nv, "mlp_gate_up_32768x34816x5120", seg_ratio=True, n_rows=16, n_cols=4096)
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
+@pytest.mark.parametrize("K", [512, 2048, 5120])
+@pytest.mark.parametrize("xdt,mode", [("bf16", "dynamic"), ("bf16", "static"), ("f32", "dynamic")])
+def test_decode_stream_shapes(nv, M, K, xdt, mode):
+    """Decode shapes on the streaming GEMV (K % 512 == 0): ragged N, several token
+    counts, both input dtypes, dynamic and static activation scales."""
+    rng = np.random.default_rng(M * 7919 + K)
+    N = 1000
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, rng.choice(K, max(1, K // 100), replace=False)] *= 60
+    bits = W._to_bf16_bits(x) if xdt == "bf16" else None
+    xv = W.bf16_bits_to_f32(bits) if xdt == "bf16" else x
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wl = W.Workload(name="decode", M=M, N=N, K=K, x_dtype=xdt, y_dtype="bf16", seg_end=[300, N],
+                    seg_sigma=[0.02, 0.02], n_hot=1, hot_gain=(60, 60))
+    wl.data.update(x32=x, w32=w)
+    if bits is not None:
+        wl.data["x_bf16"] = bits
+    act = 0.05 if mode == "static" else None
+    r = _run_layer(nv, wl, use_linear=True, act_static=act)
+    yref, _, bound = _oracle_side(wl, r, act_static=act)
+    P.assert_within_tolerance(P.y_to_f64(r["y"]), yref, bound, f"decode M={M} K={K} {xdt} {mode}")
