@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 NVFP4 GEMM TFLOPS incl. act-quant (M=8192,K=5120); decode GB/s"
 PEAK_MFMA_F16_TFLOPS = 2500.0          # MI355X dense f16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0                 # MI355X HBM3E
+OTHER_WORKLOADS = ["gdn_gates_32768x96x5120", "mlp_gate_up_32768x34816x5120"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gdn_in_proj_traffic.json")
 KERNEL_SOURCES = ["nvfp4_w4a4_quantized_amd/csrc/gemm.hip", "nvfp4_w4a4_quantized_amd/csrc/nvfp4_device.hpp",
                   "nvfp4_w4a4_quantized_amd/csrc/launch.hpp"]
@@ -161,6 +162,76 @@ def time_decode(nv, steps, warmup):
                 timing="back-to-back calls, rotated weight copies, one event pair around all calls")
 
 
+def time_config(nv, name, steps, warmup):
+    """Another prefill-shaped workload, timed like the headline: one step =
+    nvfp4_quantize_act (calibrated activation scale) + nvfp4_w4a4_gemm, with
+    HIP events around each launch on the launch stream.  Calibrated weight
+    scales (segment scales 4x apart) are derived on the GPU: segment 0 is packed
+    once in dynamic mode and its amax-derived scale is read back."""
+    import torch
+    from synth import workloads as W
+    wl = W.generate(name)
+    seg_g = None
+    if wl.seg_scale_ratio is not None:
+        _, _, _, wg0 = setup_layer(nv, wl)
+        g0 = float(wg0[0].item())
+        seg_g = [float(np.float32(r) * np.float32(g0)) for r in wl.seg_scale_ratio]
+        del wg0
+    xt, wc, ws, wg = setup_layer(nv, wl, seg_g)
+    wl.data.pop("w32", None)
+    wl.data.pop("x32", None)
+    M, N, K = wl.M, wl.N, wl.K
+    gate = None
+    if wl.gate_heads:
+        gate = (torch.from_numpy(wl.data["A_log"]).cuda(), torch.from_numpy(wl.data["dt_bias"]).cuda())
+    gstat = torch.empty(1, dtype=torch.float32, device="cuda")
+    ac, as_ = nv.empty_packed(M, K, "cuda")
+    nv.nvfp4_quantize_act(xt, None, ac, as_, gstat)
+    y = torch.empty((M, N), dtype=torch.bfloat16 if wl.y_dtype == "bf16" else torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    gout = torch.empty(1, dtype=torch.float32, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        nv.nvfp4_quantize_act(xt, gstat, ac, as_, gout, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        nv.nvfp4_w4a4_gemm(ac, as_, gout, wc, ws, wl.seg_end, wg, y, gate=gate, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    flops = 2.0 * M * N * K
+    ybytes = M * N * (2 if wl.y_dtype == "bf16" else 4)
+    packed = lambda rows: rows * K // 2 + rows * K // 16
+    two_stage_bytes = M * K * 2 + 2 * packed(M) + packed(N) + ybytes      # x in, codes out, codes + W in, y out
+    fused_bytes = M * K * 2 + packed(N) + ybytes                           # x in, W in, y out
+    out = dict(workload=name, M=M, N=N, K=K, segments=wl.seg_end, mode="two-stage, static activation scale",
+               ms_per_step=round(wall, 4), tflops=round(flops / (wall * 1e-3) / 1e12, 2),
+               breakdown_ms={"quantize_act": round(q_ms, 4), "gemm": round(g_ms, 4)},
+               algorithmic_bytes={"two_stage": two_stage_bytes, "fused_minimum": fused_bytes})
+    if wl.gate_heads:
+        gbps = fused_bytes / (wall * 1e-3) / 1e9
+        out.update(bound="hbm", gbps_vs_fused_minimum=round(gbps, 1), frac_hbm=round(gbps / PEAK_HBM_GBPS, 4))
+    else:
+        out.update(bound="mfma", frac_mfma=round(flops / (wall * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
+                   gemm_tflops=round(flops / (g_ms * 1e-3) / 1e12, 2))
+    del xt, wc, ws, ac, as_, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(wl, static_g, target_s=10.0):
     """The oracle as it stands, timed on the host on a bounded row sample of the
     headline workload: quantize the sampled rows of X, dequantize-then-GEMM in
@@ -202,6 +273,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dynamic", action="store_true")
     ap.add_argument("--decode-only", action="store_true", help="time only the decode GEMV (no JSON contract line)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the GDN-gates and MLP gate/up workloads")
+    ap.add_argument("--configs-only", action="store_true", help="time only the GDN-gates and MLP gate/up workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this layer is benchmarked on a single MI355X; "
@@ -215,6 +288,10 @@ def main():
     torch.cuda.set_device(0)
     if args.decode_only:
         print(json.dumps({"decode": time_decode(nv, args.steps, args.warmup)}), flush=True)
+        return
+    if args.configs_only:
+        print(json.dumps({"other_workloads": [time_config(nv, n, args.steps, args.warmup) for n in OTHER_WORKLOADS]}),
+              flush=True)
         return
     log("generating the GDN in_proj workload (8192 x 16384 x 5120)")
     wl = W.generate("gdn_in_proj_8192x16384x5120")
@@ -265,6 +342,11 @@ def main():
     if not args.no_decode:
         log("timing decode GEMV (4 x 16384 x 5120)")
         out["decode"] = time_decode(nv, args.steps, args.warmup)
+    if not args.no_configs:
+        out["other_workloads"] = []
+        for n in OTHER_WORKLOADS:
+            log(f"timing {n}")
+            out["other_workloads"].append(time_config(nv, n, args.steps, args.warmup))
     if not args.no_cpu:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(wl, np.float32(gstat.item()))

@@ -158,10 +158,10 @@ hipError_t enqueue_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t 
   one.end[0] = M;
   hipError_t e;
   const float* gvec;
+  float* gcopy = nullptr;
   if (gscale_in) {
-    e = nvfp4::launch_copy_scalar(gscale_in, gscale_out, s);
-    if (e != hipSuccess) return e;
     gvec = gscale_in;
+    gcopy = gscale_out;            // the quantizer hands the static scale back
   } else {
     e = nvfp4::launch_fill(gscale_out, 1, nullptr, s);
     if (e != hipSuccess) return e;
@@ -169,7 +169,7 @@ hipError_t enqueue_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t 
     if (e != hipSuccess) return e;
     gvec = gscale_out;
   }
-  return nvfp4::launch_quant_rows(x, in_type(x_dtype), M, K, ldx, gvec, one, codes, scales, s);
+  return nvfp4::launch_quant_rows(x, in_type(x_dtype), M, K, ldx, gvec, one, codes, scales, gcopy, s);
 }
 
 // The fused decode GEMV holds x as f16 in LDS: M * K * 2 bytes.
@@ -230,7 +230,7 @@ int32_t nvfp4_pack_weight(const void* w, int32_t w_dtype, int64_t N, int64_t K, 
       start = seg.end[i];
     }
   }
-  if (e == hipSuccess) e = nvfp4::launch_quant_rows(w, in_type(w_dtype), N, K, ldw, seg_gscale_out, seg, codes, scales, s);
+  if (e == hipSuccess) e = nvfp4::launch_quant_rows(w, in_type(w_dtype), N, K, ldw, seg_gscale_out, seg, codes, scales, nullptr, s);
   return hip_status(e, "nvfp4_pack_weight launch");
 }
 

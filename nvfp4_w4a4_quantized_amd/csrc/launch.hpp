@@ -30,10 +30,11 @@ enum class OutType : int { F32 = 0, BF16 = 1 };
 hipError_t launch_fill(float* dst, int n, const SegTable* vals_or_null, hipStream_t s);
 hipError_t launch_amax_gscale(const void* x, InType t, int64_t rows, int64_t K, int64_t ld,
                               float* gscale_out, hipStream_t s);
+// Quantize rows x K with the global scale gvec[segment(row)]; when gcopy is not
+// NULL, gvec[0] is also copied there (the static-mode scale handed back).
 hipError_t launch_quant_rows(const void* x, InType t, int64_t rows, int64_t K, int64_t ld,
                              const float* gvec, const SegTable& seg,
-                             uint8_t* codes, uint8_t* scales, hipStream_t s);
-hipError_t launch_copy_scalar(const float* src, float* dst, hipStream_t s);
+                             uint8_t* codes, uint8_t* scales, float* gcopy, hipStream_t s);
 
 // gemm.hip
 struct GemmArgs {
