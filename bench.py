@@ -191,13 +191,20 @@ def time_config(nv, name, steps, warmup):
     stream = torch.cuda.current_stream()
     gout = torch.empty(1, dtype=torch.float32, device="cuda")
 
+    fused = N <= 128 and K % 256 == 0          # the fused skinny-N linear: x read once
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        nv.nvfp4_quantize_act(xt, gstat, ac, as_, gout, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        nv.nvfp4_w4a4_gemm(ac, as_, gout, wc, ws, wl.seg_end, wg, y, gate=gate, stream=stream)
+        if fused:
+            nv.nvfp4_w4a4_linear(xt, gstat, gout, wc, ws, wl.seg_end, wg, y, gate=gate, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        else:
+            nv.nvfp4_quantize_act(xt, gstat, ac, as_, gout, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            nv.nvfp4_w4a4_gemm(ac, as_, gout, wc, ws, wl.seg_end, wg, y, gate=gate, stream=stream)
         if ev is not None:
             ev[2].record(stream)
 
@@ -217,13 +224,18 @@ def time_config(nv, name, steps, warmup):
     packed = lambda rows: rows * K // 2 + rows * K // 16
     two_stage_bytes = M * K * 2 + 2 * packed(M) + packed(N) + ybytes      # x in, codes out, codes + W in, y out
     fused_bytes = M * K * 2 + packed(N) + ybytes                           # x in, W in, y out
-    out = dict(workload=name, M=M, N=N, K=K, segments=wl.seg_end, mode="two-stage, static activation scale",
+    mode = ("fused quantize + GEMM (nvfp4_w4a4_linear), static activation scale" if fused
+            else "two-stage, static activation scale")
+    breakdown = {"linear": round(q_ms, 4)} if fused else {"quantize_act": round(q_ms, 4), "gemm": round(g_ms, 4)}
+    out = dict(workload=name, M=M, N=N, K=K, segments=wl.seg_end, mode=mode,
                ms_per_step=round(wall, 4), tflops=round(flops / (wall * 1e-3) / 1e12, 2),
-               breakdown_ms={"quantize_act": round(q_ms, 4), "gemm": round(g_ms, 4)},
+               breakdown_ms=breakdown,
                algorithmic_bytes={"two_stage": two_stage_bytes, "fused_minimum": fused_bytes})
-    if wl.gate_heads:
+    if fused:
         gbps = fused_bytes / (wall * 1e-3) / 1e9
-        out.update(bound="hbm", gbps_vs_fused_minimum=round(gbps, 1), frac_hbm=round(gbps / PEAK_HBM_GBPS, 4))
+        kgbps = fused_bytes / (q_ms * 1e-3) / 1e9
+        out.update(bound="hbm", gbps_vs_fused_minimum=round(gbps, 1), frac_hbm=round(gbps / PEAK_HBM_GBPS, 4),
+                   kernel_gbps=round(kgbps, 1), kernel_frac_hbm=round(kgbps / PEAK_HBM_GBPS, 4))
     else:
         out.update(bound="mfma", frac_mfma=round(flops / (wall * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
                    gemm_tflops=round(flops / (g_ms * 1e-3) / 1e12, 2))

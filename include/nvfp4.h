@@ -145,8 +145,10 @@ NVFP4_API int32_t nvfp4_w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scale
 /*
  * The whole layer in one call: activation quantization + GEMM + epilogues.
  * Results equal nvfp4_quantize_act followed by nvfp4_w4a4_gemm.  Decode shapes
- * (M <= 8) and skinny shapes (N <= 128) run fused kernels that quantize x in
- * registers; other shapes run the two stages and then need a_codes_out and
+ * (M <= 8) and skinny shapes (N <= 128 with K a multiple of 256) run fused
+ * kernels that quantize x in registers and never write the activation codes to
+ * memory unless asked (in dynamic mode the skinny path first reads x once for
+ * its amax); other shapes run the two stages and then need a_codes_out and
  * a_scales_out as the place to put the quantized activations.
  *   x, x_dtype, M, K, ldx, gscale_in   as for nvfp4_quantize_act
  *   gscale_out     device, 1 fp32 (output): the activation global scale used

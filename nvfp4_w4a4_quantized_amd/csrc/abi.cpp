@@ -270,7 +270,8 @@ int32_t nvfp4_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, 
   st = check_gemm_common(M, N, K, w_codes, w_scales, n_seg, seg_end, w_seg_gscale, gate, y, y_dtype, ldy, &g);
   if (st) return st;
   const bool fused_gemv = gemv_fits(M, K, x_dtype);
-  if (!fused_gemv && !a_codes_out)
+  const bool fused_skinny = !fused_gemv && nvfp4::linear_skinny_fits(M, N, K);
+  if (!fused_gemv && !fused_skinny && !a_codes_out)
     return fail(NVFP4_ERR_INVALID_ARG,
                 "this shape (M=%lld, N=%lld, K=%lld) runs in two stages and needs a_codes_out/a_scales_out",
                 (long long)M, (long long)N, (long long)K);
@@ -288,6 +289,26 @@ int32_t nvfp4_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, 
     p.a_scales_out = a_scales_out;
     p.g = g;
     return hip_status(nvfp4::launch_gemv_fused(p, s), "nvfp4_w4a4_linear (fused decode) launch");
+  }
+  if (fused_skinny) {
+    hipError_t e = hipSuccess;
+    const float* g_used = gscale_in;
+    if (!gscale_in) {                      // dynamic mode: amax pass over x first
+      e = nvfp4::launch_fill(gscale_out, 1, nullptr, s);
+      if (e == hipSuccess) e = nvfp4::launch_amax_gscale(x, in_type(x_dtype), M, K, ldx, gscale_out, s);
+      if (e != hipSuccess) return hip_status(e, "nvfp4_w4a4_linear amax launch");
+      g_used = gscale_out;
+    }
+    nvfp4::GemvArgs p{};
+    p.x = x;
+    p.x_type = in_type(x_dtype);
+    p.ldx = ldx;
+    p.gscale_in = g_used;
+    p.gscale_out = gscale_in ? gscale_out : nullptr;
+    p.a_codes_out = a_codes_out;
+    p.a_scales_out = a_scales_out;
+    p.g = g;
+    return hip_status(nvfp4::launch_linear_skinny(p, s), "nvfp4_w4a4_linear (fused skinny) launch");
   }
   hipError_t e = enqueue_quant_act(x, x_dtype, M, K, ldx, gscale_in, a_codes_out, a_scales_out, gscale_out, s);
   if (e != hipSuccess) return hip_status(e, "nvfp4_w4a4_linear quantize launch");

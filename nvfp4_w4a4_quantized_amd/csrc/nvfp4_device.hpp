@@ -76,25 +76,46 @@ __device__ __forceinline__ ScaleConsts scale_consts(float g) {
   return c;
 }
 
-// E4M3 RNE (saturating) of an fp32 t >= 0 with integer arithmetic.
-__device__ __forceinline__ uint32_t e4m3_rne_from_f32(float t) {
-  if (!(t < 448.0f)) return 0x7Eu;
-  if (t < 0x1p-6f) {                                   // subnormal E4M3: multiples of 2^-9
-    return (uint32_t)__builtin_rintf(t * 512.0f);      // exact scaling; RNE; 8 -> 0x08
+// E4M3 byte of t near a 5-significant-bit value, decided exactly (normal E4M3 range,
+// t < 448).  v = t' rounded to 5 significant bits.  If v has only 4 (an E4M3 value),
+// t rounds to v.  Otherwise v is the midpoint of two E4M3 neighbours and the sign of
+// a - 6 v g (one fma: 6 v has <= 7 significant bits, so 6 v * g + a is rounded once
+// and keeps its sign) says on which side of v the exact t = a / (6 g) lies; a tie goes
+// to the neighbour with the even mantissa.
+__device__ __forceinline__ uint32_t e4m3_byte_near(float a, float g, uint32_t tb) {
+  const uint32_t vb = (tb + 0x40000u) & 0xFFF80000u;
+  uint32_t chosen = vb;
+  if ((vb >> 19) & 1u) {
+    const float v = __uint_as_float(vb);
+    const float r = __builtin_fmaf(-(6.0f * v), g, a);
+    const uint32_t downb = vb & ~0x80000u, upb = downb + 0x100000u;
+    chosen = (r > 0.0f) ? upb : ((r < 0.0f) ? downb : (((downb >> 20) & 1u) ? upb : downb));
   }
-  uint32_t b = __float_as_uint(t);
-  b += 0x7FFFFu + ((b >> 20) & 1u);                    // RNE to 3 mantissa bits
-  return ((((b >> 23) & 0xFFu) - 120u) << 3) | ((b >> 20) & 7u);
+  const uint32_t byte = (chosen >> 20) - (120u << 3);
+  return (__uint_as_float(chosen) < 448.0f) ? byte : 0x7Eu;
 }
 
-// Exact E4M3 block-scale byte (fast path with an exact fallback near midpoints).
+// Exact E4M3 block-scale byte.  The fast path is branch-free (selects only).  When
+// t' is within 8 ulps of a 5-significant-bit value (which every E4M3 midpoint is),
+// the byte is decided exactly by e4m3_byte_near in the normal E4M3 range and by the
+// float64 reference outside it (subnormal scales, extreme global scales: rare).
+// a == 0 or g == 0 gives t == 0 -> byte 0.
 __device__ __forceinline__ uint32_t block_scale_byte(float a, const ScaleConsts& c) {
   const float t = a * c.inv6g;
-  const uint32_t key = (__float_as_uint(t) + 8u) & 0x7FFFFu;     // near a <= 4-bit value?
-  if (key <= 16u || !(t < 0x1p100f) || (t < 0x1p-100f && t != 0.0f)) return block_scale_byte_exact(a, c.g);
-  if (!(a > 0.0f) || !(c.g > 0.0f)) return 0u;
-  if (t <= 0x1p-10f) return 0u;
-  return e4m3_rne_from_f32(t);
+  const uint32_t tb = __float_as_uint(t);
+  const uint32_t b = tb + 0x7FFFFu + ((tb >> 20) & 1u);           // RNE to 3 mantissa bits
+  uint32_t r = (b >> 20) - (120u << 3);                          // ((exp - 120) << 3) | m3
+  const uint32_t sub = (uint32_t)__builtin_rintf(t * 512.0f);    // subnormal E4M3: multiples of 2^-9
+  r = (t < 0x1p-6f) ? sub : r;
+  r = (t < 448.0f) ? r : 0x7Eu;                                  // saturate at 448
+  r = (t <= 0x1p-10f) ? 0u : r;                                  // nearer to 0 (tie -> even 0)
+  const uint32_t key = (tb + 8u) & 0x7FFFFu;                     // near a 5-bit value?
+  const bool extreme = !(t < 0x1p100f) || (t < 0x1p-100f && t != 0.0f) || !(c.g >= 0x1p-120f);
+  if (key <= 16u || extreme) {
+    if (!extreme && t >= 0x1p-5f && t < 448.0f) r = e4m3_byte_near(a, c.g, tb);
+    else r = block_scale_byte_exact(a, c.g);
+  }
+  return r;
 }
 
 __device__ __forceinline__ uint32_t block_scale_byte(float a, float g) {
@@ -110,41 +131,102 @@ __device__ __forceinline__ uint32_t e2m1_code_exact(float x, double h) {
   return c | ((__float_as_uint(x) >> 28) & 8u);
 }
 
+// Per-block constants of the code computation: y = x * rh with rh = rcp(s g).
+struct BlockConsts {
+  float s;        // decoded block scale
+  float rh;       // rcp(s g) (<= 1 ulp), 0 for a zero block: codes keep only the sign
+  bool zero;      // block scale 0 or global scale 0: magnitude codes 0
+  bool fast_ok;   // s g and 1/(s g) are normal fp32 values
+};
+
+__device__ __forceinline__ BlockConsts block_consts(uint32_t sb, float g) {
+  BlockConsts b;
+  b.s = e4m3_to_f32(sb);
+  const float h32 = b.s * g;
+  b.zero = (sb == 0u) || !(g > 0.0f);
+  b.fast_ok = b.zero || (h32 >= 0x1p-120f && h32 <= 0x1p120f);
+  b.rh = b.zero ? 0.0f : __builtin_amdgcn_rcpf(h32);
+  return b;
+}
+
+// key(y) = low 21 mantissa bits of y + 16, moved to the top: < 33 << 11 iff y is
+// within 16 ulps of a value whose low 21 mantissa bits are zero (every E2M1 midpoint)
+__device__ __forceinline__ uint32_t near_key(float y) { return (__float_as_uint(y) << 11) + (16u << 11); }
+
+// Exact E2M1 code of x whose fast quotient y = x * rcp(s g) lies within 16 ulps of a
+// value v with <= 3 significant bits (every E2M1 midpoint is one).  The exact
+// quotient q = |x| / (s g) is within ~20 ulps of v, so its code is one of the codes
+// on either side of v: those of v (1 -/+ 2^-11), found with one packed conversion
+// (equal unless v is a midpoint).  The sign of |x| - v s g, from one fma (v s has
+// <= 7 significant bits, so v s * g + |x| is rounded once and keeps its sign),
+// picks between them; an exact tie goes to the even code.  Requires s g normal.
+__device__ __forceinline__ uint32_t e2m1_code_near(float x, float y, float s, float g) {
+  const float ax = __builtin_fabsf(x);
+  const float v = __uint_as_float((__float_as_uint(__builtin_fabsf(y)) + 0x100000u) & 0xFFE00000u);
+  const uint32_t cc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v * 0.99951171875f, v * 1.00048828125f, 1.0f, 0);
+  const uint32_t down = cc & 7u, up = (cc >> 4) & 7u;
+  const float r = __builtin_fmaf(-(v * s), g, ax);
+  const uint32_t mag = (r > 0.0f) ? up : ((r < 0.0f) ? down : ((down & 1u) ? up : down));
+  return mag | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+// Codes of n consecutive values v[0..n) of one block (n = 8 or 16) into w[n/8]
+// (element 0 in the low nibble of w[0]).  Elements whose fast quotient is within 16
+// ulps of a <= 3-significant-bit value are decided exactly, one by one
+// (e2m1_code_near); the float64 recomputation of the whole block is left for blocks
+// whose s g or 1/(s g) is not a normal fp32 value (extreme scales).  The empty asm
+// makes s opaque there, so the compiler cannot hoist the float64 product into the
+// common path.
+template <int NV>
+__device__ __forceinline__ void quant_block(const float v[NV], const BlockConsts& b, float g, uint32_t w[NV / 8]) {
+  float y[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) y[i] = v[i] * b.rh;
+#pragma unroll
+  for (int d = 0; d < NV / 8; ++d) {
+    uint32_t x = 0;
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * d + 0], y[8 * d + 1], 1.0f, 0);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * d + 2], y[8 * d + 3], 1.0f, 1);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * d + 4], y[8 * d + 5], 1.0f, 2);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * d + 6], y[8 * d + 7], 1.0f, 3);
+    w[d] = x;
+  }
+  uint32_t k = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < NV; i += 2) k = min(k, min(near_key(y[i]), near_key(y[i + 1])));
+  if (b.zero) return;
+  if (!b.fast_ok) {
+    float sv = b.s;
+    asm volatile("" : "+v"(sv));
+    const double h = (double)sv * (double)g;                  // exact
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const uint32_t c = e2m1_code_exact(v[i], h);
+      w[i / 8] = (w[i / 8] & ~(0xFu << (4 * (i % 8)))) | (c << (4 * (i % 8)));
+    }
+  } else if (k < (33u << 11)) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      // |y| >= 8: saturated at 6, no midpoint near (also keeps inf out of the exact path)
+      if (near_key(y[i]) < (33u << 11) && __builtin_fabsf(y[i]) < 8.0f) {
+        const uint32_t c = e2m1_code_near(v[i], y[i], b.s, g);
+        w[i / 8] = (w[i / 8] & ~(0xFu << (4 * (i % 8)))) | (c << (4 * (i % 8)));
+      }
+    }
+  }
+}
+
 // Quantize the 8 consecutive values v[0..7] of one block (block scale byte sb,
 // global scale g).  Returns the 8 codes packed, element 0 in the low nibble.
 __device__ __forceinline__ uint32_t quant8(const float v[8], uint32_t sb, float g) {
-  const float s = e4m3_to_f32(sb);
-  const float h32 = s * g;
-  const bool zero = (sb == 0u) || !(g > 0.0f);
-  // fast path valid while s g and 1/(s g) are normal fp32 values
-  const bool fast_ok = zero || (h32 >= 0x1p-120f && h32 <= 0x1p120f);
-  const float rh = zero ? 0.0f : __builtin_amdgcn_rcpf(h32);   // <= 1 ulp; 0 keeps only the sign
-  float y[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = v[i] * rh;
-  uint32_t w = 0;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
-  // key(y) = low 21 mantissa bits of y + 16, moved to the top: < 33 << 11 iff y is
-  // within 16 ulps of a value whose low 21 mantissa bits are zero
-  uint32_t k = 0xFFFFFFFFu;
-#pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    const uint32_t k0 = (__float_as_uint(y[i]) << 11) + (16u << 11);
-    const uint32_t k1 = (__float_as_uint(y[i + 1]) << 11) + (16u << 11);
-    k = min(k, min(k0, k1));
-  }
-  if (!zero && (k < (33u << 11) || !fast_ok)) {
-    const double h = (double)s * (double)g;                   // exact
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t c = e2m1_code_exact(v[i], h);
-      w = (w & ~(0xFu << (4 * i))) | (c << (4 * i));
-    }
-  }
-  return w;
+  uint32_t w[1];
+  quant_block<8>(v, block_consts(sb, g), g, w);
+  return w[0];
+}
+
+// Quantize the 16 values of one block: codes of elements 0-7 in w[0], 8-15 in w[1].
+__device__ __forceinline__ void quant16(const float v[16], uint32_t sb, float g, uint32_t w[2]) {
+  quant_block<16>(v, block_consts(sb, g), g, w);
 }
 
 // 8 packed codes (one dword) + E4M3 scale byte -> 8 f16 values e2m1 * s (exact:

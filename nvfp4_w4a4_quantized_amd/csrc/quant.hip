@@ -111,10 +111,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(const void* __restrict_
       for (int i = 1; i < 16; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
       const ScaleConsts sc = sc_lds[seg.n > 1 ? seg_of(seg, row[u] < rows ? row[u] : 0) : 0];
       const uint32_t sb = block_scale_byte(a, sc);
-      const uint32_t w0 = quant8(v, sb, sc.g);
-      const uint32_t w1 = quant8(v + 8, sb, sc.g);
+      uint32_t w[2];
+      quant16(v, sb, sc.g, w);
       if (valid[u]) {
-        *reinterpret_cast<uint2*>(codes + row[u] * (K >> 1) + (int64_t)blk[u] * 8) = uint2{w0, w1};
+        *reinterpret_cast<uint2*>(codes + row[u] * (K >> 1) + (int64_t)blk[u] * 8) = uint2{w[0], w[1]};
         scales[row[u] * (K >> 4) + blk[u]] = (uint8_t)sb;
       }
     }

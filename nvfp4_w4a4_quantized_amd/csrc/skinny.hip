@@ -1,0 +1,288 @@
+// Fused W4A4 linear for skinny N (N <= 128, K % 256 == 0): x (bf16 or fp32) is read
+// once, quantized to NVFP4 in registers and fed straight into the block-scaled
+// GEMM against the packed weight, with the per-segment / GDN-gate epilogue.  The
+// activation codes never go through HBM (unless the caller asks for them).
+//
+// This is the shape of the GDN gate projections a, b (N = 2 x 48 heads) in "Why
+// Gated DeltaNet Survives 4-Bit Quantization" (review page, mechanism step 2, Eq. 1):
+// a tall activation times a tiny weight, bound by the single read of x.
+//
+// Workgroup = 512 threads (8 waves, two per SIMD) = 128 tokens; wave w owns tokens
+// 16w .. 16w+15.  Lane (q = lane >> 4, rr = lane & 15) owns token rr and, in every
+// 128-element unit of K, the 32 elements 32q .. 32q+31: two whole 16-element blocks,
+// so the activation quantizer runs in the lane with no cross-lane step (the same
+// exact arithmetic as the stand-alone quantizer).  The lane's 32 elements feed four
+// MFMA 16x16x32 f16 steps, step t taking elements 8t .. 8t+7 of them; the weight
+// operand uses the same permutation of k, so the sum over k is unchanged.
+//
+// The weight (N x K packed, a few hundred KiB: L2-resident) is decoded exactly to
+// f16 (e2m1 x E4M3 scale) 256 K-elements at a time into a double-buffered LDS tile
+// shared by the workgroup; row stride 2 x 256 + 16 bytes keeps the per-lane 16-byte
+// reads of 32 consecutive rows on distinct banks.  x units are loaded (non-temporal:
+// read once) R - 1 units ahead of their use.
+#include "kernel_common.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int SK_THREADS = 512;                     // 8 waves, two per SIMD
+constexpr int SK_TM = 128;                          // tokens per workgroup (16 per wave)
+constexpr int SK_KC = 256;                          // K elements per decoded weight chunk
+constexpr int SK_ROWB = 2 * SK_KC + 16;             // LDS bytes per decoded weight row
+
+template <InType T> struct XUnit;                   // 32 elements of one token
+template <> struct XUnit<InType::BF16> { u32x4 q[4]; };
+template <> struct XUnit<InType::F32> { f32x4 q[8]; };
+
+template <InType T>
+__device__ __forceinline__ void xunit_load(const void* base, int64_t elem_off, XUnit<T>& r) {
+  if constexpr (T == InType::BF16) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem_off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.q[i] = __builtin_nontemporal_load(p + i);
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + elem_off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.q[i] = __builtin_nontemporal_load(p + i);
+  }
+}
+
+template <InType T>
+__device__ __forceinline__ void xunit_unpack(const XUnit<T>& r, float v[32]) {
+  if constexpr (T == InType::BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * i + 2 * e] = __uint_as_float(r.q[i][e] << 16);
+        v[8 * i + 2 * e + 1] = __uint_as_float(r.q[i][e] & 0xFFFF0000u);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * i + e] = r.q[i][e];
+  }
+}
+
+// Weight chunk staging: NT*16 rows x 32 octets (8 elements) per chunk, NT octets per
+// thread; octet index o = e * 512 + tid -> row o >> 5, octet o & 31.  Loads are
+// unconditional (rows past N re-read row N - 1; wchunk_store zeroes them): with no
+// load under a branch, the compiler counts the loads in flight exactly and never
+// has to drain the x stream.
+template <int NT>
+struct WStage {
+  uint32_t code[NT];
+  uint32_t scale[NT];
+};
+
+template <int NT>
+__device__ __forceinline__ void wchunk_load(const GemmArgs& a, int64_t c, WStage<NT>& w) {
+  const int64_t kh = a.K >> 1, kb = a.K >> 4;
+#pragma unroll
+  for (int e = 0; e < NT; ++e) {
+    const int o = e * SK_THREADS + (int)threadIdx.x;
+    const int64_t row = min<int64_t>(o >> 5, a.N - 1);
+    const int oct = o & 31;
+    w.code[e] = *reinterpret_cast<const uint32_t*>(a.w_codes + row * kh + c * (SK_KC / 2) + oct * 4);
+    w.scale[e] = a.w_scales[row * kb + c * (SK_KC / 16) + (oct >> 1)];
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void wchunk_store(uint8_t* buf, const WStage<NT>& w, int64_t N) {
+#pragma unroll
+  for (int e = 0; e < NT; ++e) {
+    const int o = e * SK_THREADS + (int)threadIdx.x;
+    const bool live = (o >> 5) < N;
+    const f16x8 d = decode8_f16(live ? w.code[e] : 0u, scale_f16x2(live ? w.scale[e] : 0u));
+    *reinterpret_cast<f16x8*>(buf + (o >> 5) * SK_ROWB + (o & 31) * 16) = d;
+  }
+}
+
+// No load or store of the main loop sits under a data-dependent branch (vmcnt counts
+// both on gfx950): the compiler then knows exactly how many are in flight and only
+// waits for the unit it is about to use.
+template <InType T, int NT, int EPI, bool CODES>
+__global__ __launch_bounds__(SK_THREADS, 1) void k_linear_skinny(GemvArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t sk_lds[];   // 2 x NT*16 rows x SK_ROWB
+  constexpr int R = (T == InType::BF16) ? 4 : 2;                     // x units in the register ring
+  constexpr int WBUF = NT * 16 * SK_ROWB;
+  const GemmArgs& a = p.g;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int q = lane >> 4, rr = lane & 15;
+  const int64_t M = a.M, K = a.K;
+  const int64_t m0 = (int64_t)blockIdx.x * SK_TM;
+  const int64_t tok = m0 + wave * 16 + rr;
+  const int64_t trow = tok < M ? tok : M - 1;                        // clamped: in bounds, never stored
+  const float g = *p.gscale_in;
+  const ScaleConsts sc = scale_consts(g);
+  if (blockIdx.x == 0 && tid == 0 && p.gscale_out != nullptr) *p.gscale_out = g;
+
+  const int64_t nu = K / 128;                                        // 128-element units
+  const int64_t xoff = trow * p.ldx + 32 * q;
+  XUnit<T> xr[R];
+#pragma unroll
+  for (int i = 0; i < R - 1; ++i) xunit_load<T>(p.x, xoff + 128 * min<int64_t>(i, nu - 1), xr[i]);
+
+  // weight chunk 0 into buffer 0 (chunk c + 1 is loaded at the start of chunk c)
+  WStage<NT> ws;
+  wchunk_load<NT>(a, 0, ws);
+  wchunk_store<NT>(sk_lds, ws, a.N);
+  const int64_t nc = K / SK_KC;
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // per-column epilogue constants, loaded once up front (all loads issued together)
+  float alpha[NT], neg_ea[NT], db[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int64_t n = min<int64_t>(16 * j + rr, a.N - 1);
+    alpha[j] = g * a.w_seg_gscale[seg_of_col(a.seg, n)];
+    if constexpr (EPI == EPI_GATE) {
+      const int64_t nh = n < a.gate.n_heads ? n : 0;
+      neg_ea[j] = a.gate.A_log[nh];
+      db[j] = a.gate.dt_bias[nh];
+    }
+  }
+
+  // B operand: weight row 16 j + rr, chunk column 128 (u % 2) + 32 q + 8 t
+  const uint32_t bbase = (uint32_t)(rr * SK_ROWB + 64 * q);
+
+  for (int64_t u0 = 0; u0 < nu; u0 += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t u = u0 + r;
+      if (u >= nu) break;                                            // uniform
+      const int64_t c = u >> 1;                                      // weight chunk
+      if (r % 2 == 0) {
+        // chunk boundary: chunk c was decoded into buffer c & 1 during chunk c - 1
+        // (chunk 0: before the loop); the barrier publishes it and ends every wave's
+        // reads of buffer (c+1) & 1.  Stage chunk c + 1 (the last chunk again at the end).
+        __syncthreads();
+        wchunk_load<NT>(a, min<int64_t>(c + 1, nc - 1), ws);
+      }
+      // keep R - 1 units of x in flight (past the end: re-read the last unit)
+      xunit_load<T>(p.x, xoff + 128 * min<int64_t>(u + R - 1, nu - 1), xr[(r + R - 1) % R]);
+
+      // quantize the lane's two blocks (elements 32q .. 32q+31 of unit u)
+      float v[32];
+      xunit_unpack<T>(xr[r], v);
+      uint32_t sb[2], w[4];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float am = __builtin_fabsf(v[16 * b]);
+#pragma unroll
+        for (int e = 1; e < 16; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(v[16 * b + e]));
+        sb[b] = block_scale_byte(am, sc);
+        quant16(v + 16 * b, sb[b], g, w + 2 * b);
+      }
+      if constexpr (CODES) {
+        // lanes past M quantized row M - 1 (trow) and store the same bytes there
+        *reinterpret_cast<u32x4*>(p.a_codes_out + trow * (K >> 1) + u * 64 + 16 * q) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<uint16_t*>(p.a_scales_out + trow * (K >> 4) + u * 8 + 2 * q) =
+            (uint16_t)(sb[0] | (sb[1] << 8));
+      }
+      // MFMA 16x16x32 steps: A = the lane's elements 8t .. 8t+7, B = weight rows
+      // 16 j + rr at the same K positions
+      const uint8_t* bl = sk_lds + (c & 1) * WBUF + bbase + 256 * (u & 1);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // all of this step's weight reads first, the decode of A under them
+        f16x8 B[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) B[j] = *reinterpret_cast<const f16x8*>(bl + j * 16 * SK_ROWB + 16 * t);
+        const f16x8 A = decode8_f16(w[t], scale_f16x2(sb[t >> 1]));
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[j], acc[j], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NT, 0);     // the NT LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);      // the A decode
+        __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);     // the NT MFMAs
+      }
+      if (r % 2 == 1) {
+        // decode the next weight chunk into the other buffer (free since the last barrier)
+        if (c + 1 < nc) wchunk_store<NT>(sk_lds + ((c + 1) & 1) * WBUF, ws, a.N);
+      }
+    }
+  }
+
+  // D (16 x 16) of tile j: lane (q, rr) holds tokens 4q .. 4q+3 of the wave, column 16 j + rr
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int64_t n = 16 * j + rr;
+    const bool n_ok = n < a.N;
+    if constexpr (EPI == EPI_GATE) {
+      // Eq. 1: g = -exp(A_log) softplus(a + dt_bias) for the a-heads, beta = sigmoid(b)
+      const bool is_a = n < a.gate.n_heads;
+      const float nea = -expf(neg_ea[j]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + wave * 16 + 4 * q + i;
+        const float v = acc[j][i] * alpha[j];
+        const float o = is_a ? nea * softplus_f32(v + db[j]) : sigmoid_f32(v);
+        if (n_ok && m < M) reinterpret_cast<float*>(a.y)[m * a.ldy + n] = o;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + wave * 16 + 4 * q + i;
+        if (n_ok && m < M) store_out<EPI>(a, m, n, acc[j][i], alpha[j]);
+      }
+    }
+  }
+}
+
+template <InType T, int NT, int EPI, bool CODES>
+hipError_t launch_ntc(const GemvArgs& p, hipStream_t s) {
+  static bool attr_set = false;
+  const size_t lds = 2 * (size_t)NT * 16 * SK_ROWB;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_linear_skinny<T, NT, EPI, CODES>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const unsigned grid = (unsigned)((p.g.M + SK_TM - 1) / SK_TM);
+  hipLaunchKernelGGL((k_linear_skinny<T, NT, EPI, CODES>), dim3(grid), dim3(SK_THREADS), lds, s, p);
+  return hipGetLastError();
+}
+
+template <InType T, int NT, int EPI>
+hipError_t launch_nt(const GemvArgs& p, hipStream_t s) {
+  return p.a_codes_out != nullptr ? launch_ntc<T, NT, EPI, true>(p, s) : launch_ntc<T, NT, EPI, false>(p, s);
+}
+
+// NT = number of 16-column weight tiles, rounded up to an even count
+template <InType T, int EPI>
+hipError_t launch_t(const GemvArgs& p, hipStream_t s) {
+  switch ((int)((p.g.N + 31) / 32)) {
+    case 1: return launch_nt<T, 2, EPI>(p, s);
+    case 2: return launch_nt<T, 4, EPI>(p, s);
+    case 3: return launch_nt<T, 6, EPI>(p, s);
+    default: return launch_nt<T, 8, EPI>(p, s);
+  }
+}
+
+template <InType T>
+hipError_t launch_epi(const GemvArgs& p, hipStream_t s) {
+  if (p.g.gate.n_heads > 0) return launch_t<T, EPI_GATE>(p, s);
+  if (p.g.y_type == OutType::BF16) return launch_t<T, EPI_BF16>(p, s);
+  return launch_t<T, EPI_F32>(p, s);
+}
+
+}  // namespace
+
+bool linear_skinny_fits(int64_t M, int64_t N, int64_t K) {
+  return N >= 1 && N <= 128 && K % SK_KC == 0 && K > 0 && M >= 1;
+}
+
+hipError_t launch_linear_skinny(const GemvArgs& p, hipStream_t s) {
+  return p.x_type == InType::BF16 ? launch_epi<InType::BF16>(p, s) : launch_epi<InType::F32>(p, s);
+}
+
+}  // namespace nvfp4

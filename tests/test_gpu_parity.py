@@ -408,3 +408,83 @@ def test_decode_stream_shapes(nv, M, K, xdt, mode):
     r = _run_layer(nv, wl, use_linear=True, act_static=act)
     yref, _, bound = _oracle_side(wl, r, act_static=act)
     P.assert_within_tolerance(P.y_to_f64(r["y"]), yref, bound, f"decode M={M} K={K} {xdt} {mode}")
+
+
+def _skinny_case(M, N, seg_end, K, xdt, seed, gate_heads=0, y_dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, rng.choice(K, max(1, K // 100), replace=False)] *= 50
+    bits = W._to_bf16_bits(x) if xdt == "bf16" else None
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wl = W.Workload(name="skinny", M=M, N=N, K=K, x_dtype=xdt, y_dtype=y_dtype, seg_end=seg_end,
+                    seg_sigma=[0.02] * len(seg_end), n_hot=1, hot_gain=(50, 50), gate_heads=gate_heads)
+    wl.data.update(x32=x, w32=w)
+    if bits is not None:
+        wl.data["x_bf16"] = bits
+    if gate_heads:
+        wl.data["A_log"] = rng.uniform(0.0, 2.7, gate_heads).astype(np.float32)
+        wl.data["dt_bias"] = (rng.standard_normal(gate_heads) * 0.5).astype(np.float32)
+    return wl
+
+
+@pytest.mark.parametrize("M,N,seg_end,K,xdt,gate_heads,y_dtype", [
+    (300, 96, [48, 96], 5120, "bf16", 48, "f32"),      # GDN gates shape, ragged M, gate epilogue
+    (13, 17, [17], 256, "f32", 0, "bf16"),             # one chunk, one 32-column tile, fp32 input
+    (129, 128, [64, 128], 512, "bf16", 0, "bf16"),     # four column tiles, two segments
+    (200, 40, [8, 40], 768, "f32", 0, "f32"),          # three chunks, fp32 in and out
+    (9, 96, [48, 96], 1024, "bf16", 48, "f32"),        # just above the decode GEMV's token limit
+])
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("codes_out", [True, False])
+def test_linear_skinny_fused(nv, M, N, seg_end, K, xdt, gate_heads, y_dtype, mode, codes_out):
+    """The fused skinny-N linear (x read once, quantized in registers) against the
+    oracle: global scale and (when requested) codes bit-exact, outputs within the
+    GEMM tolerance."""
+    wl = _skinny_case(M, N, seg_end, K, xdt, seed=M * 31 + N * 7 + K, gate_heads=gate_heads, y_dtype=y_dtype)
+    act = 0.0457 if mode == "static" else None
+    xv, xt = _x_inputs(wl)
+    wt = P.dev_x(wl.data["w32"])
+    wc, ws, wg = P.gpu_pack(nv, wt, wl.seg_end, None)
+    y = torch.empty((M, N), dtype=torch.bfloat16 if y_dtype == "bf16" else torch.float32, device="cuda")
+    gate = None
+    if gate_heads:
+        gate = (torch.from_numpy(wl.data["A_log"]).cuda(), torch.from_numpy(wl.data["dt_bias"]).cuda())
+    gin = None if act is None else torch.tensor([act], dtype=torch.float32, device="cuda")
+    gout = torch.empty(1, dtype=torch.float32, device="cuda")
+    ac = as_ = None
+    if codes_out:
+        ac, as_ = nv.empty_packed(M, K, "cuda")
+    nv.nvfp4_w4a4_linear(xt, gin, gout, wc, ws, wl.seg_end, wg, y, gate=gate, a_codes_out=ac, a_scales_out=as_)
+    torch.cuda.synchronize()
+    oc, os_, og = O.quantize_activation(P.x64_of(xv), None if act is None else np.float32(act))
+    owc, ows, owg = O.pack_weight(wl.data["w32"].astype(np.float64), wl.seg_end)
+    assert np.float32(gout.item()) == og
+    if codes_out:
+        P.assert_bytes_equal(ac.cpu().numpy(), oc, "activation codes")
+        P.assert_bytes_equal(as_.cpu().numpy(), os_, "activation scales")
+    ogate = (wl.data["A_log"], wl.data["dt_bias"]) if gate_heads else None
+    yref, _, bound = P.oracle_reference(oc, os_, og, owc, ows, wl.seg_end, owg, y_dtype, gate=ogate)
+    P.assert_within_tolerance(P.y_to_f64(y), yref, bound, f"skinny M={M} N={N} K={K} {xdt} {mode}")
+
+
+def test_linear_skinny_equals_two_stage(nv):
+    """Fused skinny path and the two-stage path (quantize, then GEMM) agree to the
+    GEMM tolerance on the same inputs; their activation codes are identical."""
+    wl = _skinny_case(257, 96, [48, 96], 2048, "bf16", seed=11, gate_heads=48, y_dtype="f32")
+    xv, xt = _x_inputs(wl)
+    wc, ws, wg = P.gpu_pack(nv, P.dev_x(wl.data["w32"]), wl.seg_end, None)
+    gate = (torch.from_numpy(wl.data["A_log"]).cuda(), torch.from_numpy(wl.data["dt_bias"]).cuda())
+    y1 = torch.empty((257, 96), dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y1)
+    g1 = torch.empty(1, dtype=torch.float32, device="cuda")
+    g2 = torch.empty_like(g1)
+    ac1, as1 = nv.empty_packed(257, 2048, "cuda")
+    ac2, as2 = nv.empty_packed(257, 2048, "cuda")
+    nv.nvfp4_w4a4_linear(xt, None, g1, wc, ws, wl.seg_end, wg, y1, gate=gate, a_codes_out=ac1, a_scales_out=as1)
+    nv.nvfp4_quantize_act(xt, None, ac2, as2, g2)
+    nv.nvfp4_w4a4_gemm(ac2, as2, g2, wc, ws, wl.seg_end, wg, y2, gate=gate)
+    torch.cuda.synchronize()
+    assert g1.item() == g2.item()
+    assert torch.equal(ac1, ac2) and torch.equal(as1, as2)
+    a, b = y1.double(), y2.double()
+    assert float(torch.linalg.norm(a - b) / torch.linalg.norm(b)) < 1e-5
