@@ -30,9 +30,10 @@ METRIC = "W4A4 NVFP4 GEMM TFLOPS incl. act-quant (M=8192,K=5120); decode GB/s"
 PEAK_MFMA_F16_TFLOPS = 2500.0          # MI355X dense f16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0                 # MI355X HBM3E
 OTHER_WORKLOADS = ["gdn_gates_32768x96x5120", "mlp_gate_up_32768x34816x5120"]
+COPY_BYTES = 256 << 20                 # calibration copy for the HBM byte counters
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gdn_in_proj_traffic.json")
-KERNEL_SOURCES = ["nvfp4_w4a4_quantized_amd/csrc/gemm.hip", "nvfp4_w4a4_quantized_amd/csrc/nvfp4_device.hpp",
-                  "nvfp4_w4a4_quantized_amd/csrc/launch.hpp"]
+KERNEL_SOURCES = ["nvfp4_w4a4_quantized_amd/csrc/gemm.hip", "nvfp4_w4a4_quantized_amd/csrc/kernel_common.hpp",
+                  "nvfp4_w4a4_quantized_amd/csrc/nvfp4_device.hpp", "nvfp4_w4a4_quantized_amd/csrc/launch.hpp"]
 
 
 def log(*a):
@@ -244,6 +245,48 @@ def time_config(nv, name, steps, warmup):
     return out
 
 
+def profile_target(nv, target, launches):
+    """Launch one kernel of the path a few times and nothing else, for counter runs
+    (rocprofv3 --pmc): first a plain copy of COPY_BYTES (the calibration kernel whose
+    HBM bytes are known: COPY_BYTES read + COPY_BYTES written), then `launches`
+    launches of the target:
+      gemm   - nvfp4_w4a4_gemm on the GDN in_proj workload (8192 x 16384 x 5120)
+      quant  - nvfp4_quantize_act on the same activations (static scale)
+      decode - nvfp4_w4a4_linear, decode GEMV 4 x 16384 x 5120
+      gates  - nvfp4_w4a4_linear, fused GDN gates 32768 x 96 x 5120"""
+    import torch
+    from synth import workloads as W
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    name = {"gemm": "gdn_in_proj_8192x16384x5120", "quant": "gdn_in_proj_8192x16384x5120",
+            "decode": "decode_gemv_4x16384x5120", "gates": "gdn_gates_32768x96x5120"}[target]
+    wl = W.generate(name)
+    xt, wc, ws, wg = setup_layer(nv, wl)
+    M, N, K = wl.M, wl.N, wl.K
+    g = torch.empty(1, dtype=torch.float32, device="cuda")
+    ac, as_ = nv.empty_packed(M, K, "cuda")
+    nv.nvfp4_quantize_act(xt, None, ac, as_, g)            # calibrated scale: this tensor's own
+    y = torch.empty((M, N), dtype=torch.bfloat16 if wl.y_dtype == "bf16" else torch.float32, device="cuda")
+    gout = torch.empty(1, dtype=torch.float32, device="cuda")
+    gate = None
+    if wl.gate_heads:
+        gate = (torch.from_numpy(wl.data["A_log"]).cuda(), torch.from_numpy(wl.data["dt_bias"]).cuda())
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        if target == "gemm":
+            nv.nvfp4_w4a4_gemm(ac, as_, g, wc, ws, wl.seg_end, wg, y)
+        elif target == "quant":
+            nv.nvfp4_quantize_act(xt, g, ac, as_, gout)
+        else:
+            nv.nvfp4_w4a4_linear(xt, g, gout, wc, ws, wl.seg_end, wg, y, gate=gate)
+    torch.cuda.synchronize()
+    print(f"profile target {target}: {launches} launches of {name} after a {COPY_BYTES >> 20} MiB copy", flush=True)
+
+
 def cpu_baseline(wl, static_g, target_s=10.0):
     """The oracle as it stands, timed on the host on a bounded row sample of the
     headline workload: quantize the sampled rows of X, dequantize-then-GEMM in
@@ -287,6 +330,9 @@ def main():
     ap.add_argument("--decode-only", action="store_true", help="time only the decode GEMV (no JSON contract line)")
     ap.add_argument("--no-configs", action="store_true", help="skip the GDN-gates and MLP gate/up workloads")
     ap.add_argument("--configs-only", action="store_true", help="time only the GDN-gates and MLP gate/up workloads")
+    ap.add_argument("--profile-target", choices=["gemm", "quant", "decode", "gates"],
+                    help="for counter runs: a calibration copy, then a few launches of one kernel (no JSON line)")
+    ap.add_argument("--launches", type=int, default=3)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this layer is benchmarked on a single MI355X; "
@@ -298,6 +344,9 @@ def main():
     from synth import workloads as W
 
     torch.cuda.set_device(0)
+    if args.profile_target:
+        profile_target(nv, args.profile_target, args.launches)
+        return
     if args.decode_only:
         print(json.dumps({"decode": time_decode(nv, args.steps, args.warmup)}), flush=True)
         return

@@ -368,18 +368,75 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   ++kt;
   kstep.template operator()<false, false, 0>(kt);      // kt = nk - 1
 
+  // Epilogue.  The four column scales are loaded together (no load waits for
+  // another).  Interior tiles, which are all tiles when M and N are multiples of 256,
+  // store without per-element bounds checks through a buffer descriptor of y: the
+  // lane's part of the address is one VGPR offset fixed for the whole epilogue and the
+  // rest (row block, row, column block) is a wave-uniform SGPR offset, so a store costs
+  // no address arithmetic.  The byte extent of y must be < 2^32 (checked here); it is
+  // also the descriptor's size, past which the hardware drops stores.
+  // bf16 output is stored as 32-bit pairs of adjacent columns: rows 2p and 2p+1 of a
+  // lane's column are converted together, the pair is swapped with the neighbouring
+  // lane (DPP), and v_perm assembles [row 2p: columns c, c+1] on even lanes and
+  // [row 2p+1: columns c-1, c] on odd lanes.
   const float ga = *a.a_gscale;
+  float alpha[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + wn * 128 + j * 32 + li;
+    alpha[j] = col_alpha<EPI>(a, min<int64_t>(n, a.N - 1), ga);
+  }
+  static_assert(EPI != EPI_GATE, "the gate epilogue runs in the 128x128-tile kernel");
+  constexpr int ESZ = (EPI == EPI_BF16) ? 2 : 4;
+  const int64_t extent = ((a.M - 1) * a.ldy + a.N) * ESZ;
+  if (m0 + GBM <= a.M && n0 + GBN <= a.N && extent < (int64_t(1) << 32) && (a.ldy % 2) == 0) {
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, (int)(uint32_t)extent, 0x00020000);
+    const uint32_t ldyb = (uint32_t)a.ldy * ESZ;
+    // wave-uniform (wm, wn are per wave); readfirstlane tells the compiler so
+    const uint32_t tile_off = __builtin_amdgcn_readfirstlane((uint32_t)(m0 + wm * 128) * ldyb + (uint32_t)(n0 + wn * 128) * ESZ);
+    if constexpr (EPI == EPI_BF16) {
+      const bool odd = (li & 1) != 0;
+      const uint32_t voff = (uint32_t)(4 * h) * ldyb + (uint32_t)li * 2 + (odd ? ldyb - 2 : 0u);
+      const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int p = 0; p < 8; ++p) {
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const f32x2 v = {acc[i][j][2 * p] * alpha[j], acc[i][j][2 * p + 1] * alpha[j]};
+            const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+            const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp((int)pk, (int)pk, 0xB1, 0xF, 0xF, false);
+            const uint32_t word = __builtin_amdgcn_perm(nb, pk, sel);
+            const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (p >> 1) + 2 * (p & 1)) * ldyb + (uint32_t)(j * 64);
+            __builtin_amdgcn_raw_buffer_store_b32(word, yr, voff, soff, 0);
+          }
+    } else {
+      const uint32_t voff = (uint32_t)(4 * h) * ldyb + (uint32_t)li * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldyb + (uint32_t)(j * 128);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r] * alpha[j]), yr, voff, soff, 0);
+          }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t n = n0 + wn * 128 + j * 32 + li;
     const bool n_ok = n < a.N;
-    const float alpha = n_ok ? col_alpha<EPI>(a, n, ga) : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (n_ok && m < a.M) store_out<EPI>(a, m, n, acc[i][j][r], alpha);
+        if (n_ok && m < a.M) store_out<EPI>(a, m, n, acc[i][j][r], alpha[j]);
       }
   }
 }
