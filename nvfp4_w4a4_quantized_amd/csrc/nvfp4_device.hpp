@@ -8,18 +8,22 @@
 // Exactness.  The block scale is E4M3-RNE of t = amax_block / (6 g) and each code is
 // E2M1-RNE of |x| / (s g), both of the *exact* quotient.
 //  * Block scale: fast path t' = amax * fp32(1/(6g)) in fp32 (|t' - t| <= 2 ulp) rounded
-//    to E4M3 with integer arithmetic.  Every E4M3 midpoint (and every other value with
-//    <= 4 significant bits) has its low 19 mantissa bits zero; a t' within 8 ulps of
-//    such a value is redone exactly: one float64 division, whose result never crosses
-//    or lands on an E4M3 midpoint unless the exact quotient does (midpoints have <= 5
-//    significant bits, 6g <= 27, amax <= 24: a non-zero gap is >= ~2^-32 relative,
-//    the division error <= 2^-53).
+//    to E4M3 with integer arithmetic.  Every E4M3 midpoint has <= 5 significant bits
+//    (its low 19 mantissa bits are zero); when t' is within 8 ulps of such a value v,
+//    the side of v on which the exact t lies is the sign of amax - 6 v g, which one fma
+//    gives exactly (6 v has <= 7 significant bits, so -(6 v) is exact and the fma rounds
+//    amax - 6 v g once, which keeps its sign; g >= 2^-100 keeps every term far above
+//    the subnormal range).  Subnormal scales and extreme global scales take one
+//    float64 division instead (exact there: midpoints have <= 5 significant bits, a
+//    non-zero gap is >= ~2^-32 relative, the division error <= 2^-53).
 //  * Codes: y = x * rcp(s g) in fp32 (|y - r| <= 3 ulp(y)) converted by the hardware
 //    E2M1 RNE conversion (v_cvt_scalef32_pk_fp4_f32: exact RNE with saturation at 6,
 //    the sign of x kept, power-of-two scale 1.0).  A code can only be wrong if a
-//    midpoint lies within that distance; every midpoint has its low 21 mantissa bits
-//    zero, and any y within 16 ulps of such a value is redone exactly in float64
-//    (mu * s * g is exact there).  Rare on real data.
+//    midpoint lies within that distance; every midpoint has <= 3 significant bits (its
+//    low 21 mantissa bits are zero), and for a y within 16 ulps of such a value v the
+//    sign of |x| - v s g, again one exactly-signed fma (v s has <= 7 significant bits),
+//    picks the code.  Blocks whose s g is outside [2^-100, 2^120] are redone in float64
+//    (the product s g is exact there).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -110,7 +114,7 @@ __device__ __forceinline__ uint32_t block_scale_byte(float a, const ScaleConsts&
   r = (t < 448.0f) ? r : 0x7Eu;                                  // saturate at 448
   r = (t <= 0x1p-10f) ? 0u : r;                                  // nearer to 0 (tie -> even 0)
   const uint32_t key = (tb + 8u) & 0x7FFFFu;                     // near a 5-bit value?
-  const bool extreme = !(t < 0x1p100f) || (t < 0x1p-100f && t != 0.0f) || !(c.g >= 0x1p-120f);
+  const bool extreme = !(t < 0x1p100f) || (t < 0x1p-100f && t != 0.0f) || !(c.g >= 0x1p-100f);
   if (key <= 16u || extreme) {
     if (!extreme && t >= 0x1p-5f && t < 448.0f) r = e4m3_byte_near(a, c.g, tb);
     else r = block_scale_byte_exact(a, c.g);
@@ -136,7 +140,8 @@ struct BlockConsts {
   float s;        // decoded block scale
   float rh;       // rcp(s g) (<= 1 ulp), 0 for a zero block: codes keep only the sign
   bool zero;      // block scale 0 or global scale 0: magnitude codes 0
-  bool fast_ok;   // s g and 1/(s g) are normal fp32 values
+  bool fast_ok;   // s g in [2^-100, 2^120]: 1/(s g) is normal and the exact-sign fma
+                  // of e2m1_code_near stays clear of the subnormal range
 };
 
 __device__ __forceinline__ BlockConsts block_consts(uint32_t sb, float g) {
@@ -144,7 +149,7 @@ __device__ __forceinline__ BlockConsts block_consts(uint32_t sb, float g) {
   b.s = e4m3_to_f32(sb);
   const float h32 = b.s * g;
   b.zero = (sb == 0u) || !(g > 0.0f);
-  b.fast_ok = b.zero || (h32 >= 0x1p-120f && h32 <= 0x1p120f);
+  b.fast_ok = b.zero || (h32 >= 0x1p-100f && h32 <= 0x1p120f);
   b.rh = b.zero ? 0.0f : __builtin_amdgcn_rcpf(h32);
   return b;
 }
