@@ -228,10 +228,40 @@ __global__ __launch_bounds__(GS_THREADS, 1) void k_gemv_stream(GemvArgs p) {
   const int64_t n0 = (int64_t)blockIdx.x * GS_ROWS;
   uint8_t* const sc_lds = gs_lds + M * TS;                      // [64 rows][K/16] scale bytes
 
-  // (0) the workgroup's weight scales (64 contiguous rows of K/16 bytes) straight into
+  // (0) the calibrated global scale, loaded before anything else: vmcnt counts loads
+  // in issue order, so waiting for it then waits for no other load.  The load is
+  // unconditional (from an always-valid address in dynamic mode, result unused there).
+  const float g_in = *(p.gscale_in ? p.gscale_in : a.w_seg_gscale);
+  asm volatile("" ::: "memory");
+
+  // (1) x loads first (the quantization waits for them, and vmcnt counts in issue
+  // order): chunk c = i * 512 + tid, 8 elements each.  Chunks past the end load
+  // the last chunk again (unconditional loads: no branch, so the compiler never has
+  // to wait for a load to merge control flow); only chunks < total are used.  The row
+  // of a chunk is found by comparisons (M <= 8), not by a division.
+  const uint32_t cpr = (uint32_t)(K >> 3);         // chunks per row
+  const uint32_t total_chunks = (uint32_t)M * cpr;
+  auto chunk_row = [&](uint32_t c) {
+    uint32_t row = 0;
+#pragma unroll
+    for (int r = 1; r < 8; ++r) row += (r < M && c >= (uint32_t)r * cpr) ? 1u : 0u;
+    return row;
+  };
+  XRaw<T> xr[GS_XMAX];
+#pragma unroll
+  for (int i = 0; i < GS_XMAX; ++i) {
+    if ((uint32_t)i * GS_THREADS < total_chunks) {                // uniform across the workgroup
+      const uint32_t c = min((uint32_t)i * GS_THREADS + tid, total_chunks - 1);
+      const uint32_t row = chunk_row(c), col = (c - row * cpr) * 8u;
+      xraw_load<T>(p.x, (int64_t)row * p.ldx + col, xr[i]);
+    }
+  }
+
+  // (2a) the workgroup's weight scales (64 contiguous rows of K/16 bytes) straight into
   // LDS: 16-byte units u = j * 512 + tid.  Units past the last row clamp their source
-  // (in bounds; those rows are never stored).  Issued first, so that waiting for any
-  // later load also waits for them.
+  // (in bounds; those rows are never stored).  Issued after x and before the codes:
+  // the x quantization waits for x only, and waiting for any code also waits for them.
+  asm volatile("" ::: "memory");                                 // keep the x loads first
   {
     const int64_t last = (min<int64_t>(N, n0 + GS_ROWS) - n0) * kb - 16;
 #pragma unroll
@@ -243,22 +273,7 @@ __global__ __launch_bounds__(GS_THREADS, 1) void k_gemv_stream(GemvArgs p) {
     asm volatile("" ::: "memory");
   }
 
-  // (1) x loads: chunk c = i * 512 + tid, 8 elements each
-  const uint32_t cpr = (uint32_t)(K >> 3);         // chunks per row
-  const uint32_t total_chunks = (uint32_t)M * cpr;
-  XRaw<T> xr[GS_XMAX];
-#pragma unroll
-  for (int i = 0; i < GS_XMAX; ++i) {
-    const uint32_t c = (uint32_t)i * GS_THREADS + tid;
-    if (c < total_chunks) {
-      const uint32_t row = c / cpr, col = (c - row * cpr) * 8u;
-      xraw_load<T>(p.x, (int64_t)row * p.ldx + col, xr[i]);
-    } else {
-      xr[i] = XRaw<T>{};
-    }
-  }
-
-  // (2) the weight stream of this lane: row n, eighth e = 4 * khalf + q
+  // (2b) the weight stream of this lane: row n, eighth e = 4 * khalf + q
   const int rg = wave & 3, khalf = wave >> 2;
   const int q = lane >> 4, r16 = lane & 15;
   const int64_t n = (int64_t)blockIdx.x * GS_ROWS + rg * 16 + r16;
@@ -274,15 +289,17 @@ __global__ __launch_bounds__(GS_THREADS, 1) void k_gemv_stream(GemvArgs p) {
   // (3) global scale and x quantization into LDS
   float g;
   if (p.gscale_in) {
-    g = *p.gscale_in;
+    g = g_in;
   } else {
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < GS_XMAX; ++i) {
-      float v[8];
-      xraw_unpack<T>(xr[i], v);
+      if ((uint32_t)i * GS_THREADS < total_chunks) {              // chunks that were loaded
+        float v[8];
+        xraw_unpack<T>(xr[i], v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(v[e]));
+        for (int e = 0; e < 8; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(v[e]));
+      }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) am = __builtin_fmaxf(am, __shfl_xor(am, off));
@@ -303,21 +320,22 @@ __global__ __launch_bounds__(GS_THREADS, 1) void k_gemv_stream(GemvArgs p) {
     wq[i] = 0u;
     sq[i] = 0u;
     const uint32_t c = (uint32_t)i * GS_THREADS + tid;
-    if ((uint32_t)i * GS_THREADS >= total_chunks) break;          // uniform across the workgroup
-    float xv[8];
-    xraw_unpack<T>(xr[i], xv);
-    float am = __builtin_fabsf(xv[0]);
+    if ((uint32_t)i * GS_THREADS < total_chunks) {                // uniform across the workgroup
+      float xv[8];
+      xraw_unpack<T>(xr[i], xv);
+      float am = __builtin_fabsf(xv[0]);
 #pragma unroll
-    for (int e = 1; e < 8; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(xv[e]));
-    am = __builtin_fmaxf(am, dpp_swap_adjacent(am));
-    const uint32_t sb = block_scale_byte(am, sc);
-    const uint32_t w = quant8(xv, sb, g);
-    if (c < total_chunks) {
-      const uint32_t row = c / cpr, col = (c - row * cpr) * 8u;
-      const f16x8 d = decode8_f16(w, scale_f16x2(sb));
-      *reinterpret_cast<f16x8*>(gs_lds + row * TS + 2 * (int64_t)col) = d;
-      wq[i] = w;
-      sq[i] = sb;
+      for (int e = 1; e < 8; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(xv[e]));
+      am = __builtin_fmaxf(am, dpp_swap_adjacent(am));
+      const uint32_t sb = block_scale_byte(am, sc);
+      const uint32_t w = quant8(xv, sb, g);
+      if (c < total_chunks) {
+        const uint32_t row = chunk_row(c), col = (c - row * cpr) * 8u;
+        const f16x8 d = decode8_f16(w, scale_f16x2(sb));
+        *reinterpret_cast<f16x8*>(gs_lds + row * TS + 2 * (int64_t)col) = d;
+        wq[i] = w;
+        sq[i] = sb;
+      }
     }
   }
   wait_vmcnt<NA>();        // the scale loads (issued before everything else) have landed
@@ -335,6 +353,7 @@ __global__ __launch_bounds__(GS_THREADS, 1) void k_gemv_stream(GemvArgs p) {
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     if (i + NA < NL) codes[i + NA] = __builtin_nontemporal_load(wc + 4 * (i + NA));
+    __builtin_amdgcn_sched_barrier(0);    // keep the load here: the scheduler would sink it to its use
     const f16x2 sp = scale_pair_f16(*reinterpret_cast<const uint16_t*>(srow + 8 * i));   // {block 8i+2q, +1}
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -352,7 +371,7 @@ __global__ __launch_bounds__(GS_THREADS, 1) void k_gemv_stream(GemvArgs p) {
       for (int i = 0; i < GS_XMAX; ++i) {
         const uint32_t c = (uint32_t)i * GS_THREADS + tid;
         if (c < total_chunks) {
-          const uint32_t row = c / cpr, col = (c - row * cpr) * 8u;
+          const uint32_t row = chunk_row(c), col = (c - row * cpr) * 8u;
           *reinterpret_cast<uint32_t*>(p.a_codes_out + (int64_t)row * (K >> 1) + (col >> 1)) = wq[i];
           if ((tid & 1) == 0) p.a_scales_out[(int64_t)row * (K >> 4) + (col >> 4)] = (uint8_t)sq[i];
         }
@@ -379,6 +398,249 @@ __global__ __launch_bounds__(GS_THREADS, 1) void k_gemv_stream(GemvArgs p) {
       }
     }
   }
+}
+
+
+// ---------------------------------------------------------------------------------
+// Fused decode GEMV, two wave roles (M <= 8, K % 1024 == 0).  Workgroup = 1024
+// threads = 64 weight rows.
+//  * stream waves 0-7: wave w takes rows 16*(w&3) .. +15 and half w>>2 of K, with the
+//    lane layout of k_gemv_stream.  Once x has landed they issue the first NA code
+//    loads of their stream (non-temporal: read once), wait for the quantized x, then
+//    consume the stream in arrival order (MFMA 16x16x32, tokens as B) issuing each
+//    further load NA ahead.  (x is loaded first by every workgroup: issued behind
+//    the stream it would be queued behind it.)
+//  * x waves 8-15: bring x and the workgroup's weight scales into LDS (direct-to-LDS
+//    loads), (dynamic mode) reduce the amax, and quantize x in LDS, in place, to f16
+//    e2m1 * s.  fp32 x is staged in a region of its own and quantized from there.
+// A wave that issues more loads than the memory system takes stalls at issue, and the
+// quantization is VALU work: with the roles apart, the x waves quantize while the
+// stream waves wait on their loads.  The two K halves are added through LDS.
+// ---------------------------------------------------------------------------------
+constexpr int GW_THREADS = 1024;
+constexpr int GW_STREAM = 512;     // threads of the stream waves
+constexpr int GW_XT = 512;         // threads of the x waves
+// dynamic LDS limit: 160 KiB per workgroup minus the kernel's static LDS (4 KiB + 32 B)
+constexpr int GW_LDS_MAX = 152 * 1024;
+
+// LDS bytes of the workgroup's weight scales: 64 rows x K/16 bytes, filled by
+// ceil(K / 2048) direct-to-LDS load instructions of 512 x 16 bytes
+__host__ __device__ constexpr int64_t gw_scale_bytes(int64_t K) { return ((K + 2047) / 2048) * 8192; }
+// LDS bytes: x as f16 (bf16 input is staged in place there), the weight scales, and
+// for fp32 input a staging region of M x K x 4 bytes
+__host__ __device__ constexpr int64_t gw_lds_bytes(int64_t M, int64_t K, bool f32_in) {
+  return M * gs_token_stride(K) + gw_scale_bytes(K) + (f32_in ? M * K * 4 : 0);
+}
+
+template <InType T, int NL, int NA>
+__global__ __launch_bounds__(GW_THREADS, 1) void k_gemv_ws(GemvArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t gw_lds[];
+  __shared__ float red_g[8];
+  __shared__ f32x4 red_acc[4][64];
+  const GemmArgs& a = p.g;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t M = a.M, K = a.K, N = a.N;
+  const int64_t TS = gs_token_stride(K);
+  const int64_t kb = K >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * GS_ROWS;
+  uint8_t* const sc_lds = gw_lds + M * TS;                      // [64 rows][K/16] scale bytes
+  const bool dynamic = (p.gscale_in == nullptr);
+  // calibrated global scale (a scalar load; from an always-valid address in dynamic
+  // mode, where the value is unused)
+  const float g_in = *(dynamic ? a.w_seg_gscale : p.gscale_in);
+
+  if (wave < 8) {
+    // ---- stream wave ----
+    const int rg = wave & 3, khalf = wave >> 2;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int64_t kbase = khalf * (K >> 1);                      // first element of this half
+    const int64_t nrow = n0 + rg * 16 + r16;
+    const u32x4* wc = reinterpret_cast<const u32x4*>(a.w_codes + (nrow < N ? nrow : N - 1) * (K >> 1) +
+                                                     (kbase >> 1) + 16 * q);   // row clamped: in bounds, never stored
+    u32x4 codes[NL];
+    lds_sync();                                                  // barrier X (x has landed)
+#pragma unroll
+    for (int i = 0; i < NA; ++i) codes[i] = __builtin_nontemporal_load(wc + 4 * i);
+    if (dynamic) lds_sync();                                     // barrier A (amax partials)
+    lds_sync();                                                  // barrier B (x and scales in LDS)
+
+    const int xtok = r16 % (int)M;
+    const uint8_t* xrow = gw_lds + xtok * TS + 2 * kbase + 64 * q;
+    const uint8_t* srow = sc_lds + (rg * 16 + r16) * kb + (kbase >> 4) + 2 * q;
+    f32x4 acc4[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc4[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      if (i + NA < NL) codes[i + NA] = __builtin_nontemporal_load(wc + 4 * (i + NA));
+      __builtin_amdgcn_sched_barrier(0);    // keep the load here: the scheduler would sink it to its use
+      const f16x2 sp = scale_pair_f16(*reinterpret_cast<const uint16_t*>(srow + 8 * i));   // {block 8i+2q, +1}
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f16x8 wa = decode8_f16(codes[i][t], bcast(sp, t >> 1));
+        const f16x8 xb = *reinterpret_cast<const f16x8*>(xrow + 2 * (128 * i + 8 * t));
+        acc4[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, xb, acc4[t], 0, 0, 0);
+      }
+    }
+    const f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    if (khalf) red_acc[rg][lane] = acc;
+    __syncthreads();                                             // barrier C
+    if (!khalf) {
+      float g = g_in;
+      if (dynamic) {
+        float am = red_g[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) am = __builtin_fmaxf(am, red_g[i]);
+        g = global_scale_from_amax(am);
+      }
+      const f32x4 o = red_acc[rg][lane];
+      const int tok = r16;                                       // D column = token
+      if (tok < M) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t nn = n0 + rg * 16 + 4 * q + r;
+          if (nn < N) {
+            const float alpha = g * a.w_seg_gscale[seg_of_col(a.seg, nn)];
+            if (a.gate.n_heads > 0) store_out<EPI_GATE>(a, tok, nn, acc[r] + o[r], alpha);
+            else if (a.y_type == OutType::BF16) store_out<EPI_BF16>(a, tok, nn, acc[r] + o[r], alpha);
+            else store_out<EPI_F32>(a, tok, nn, acc[r] + o[r], alpha);
+          }
+        }
+      }
+    }
+    return;
+  }
+
+  // ---- x wave ----  Thread xt handles the 16-element blocks b = i * 512 + xt; x wave v
+  // owns, for each i, the 64 consecutive blocks [i * 512 + 64 v, +64) (K % 1024 == 0:
+  // a multiple of 64 blocks per row, so never split across rows) and brings exactly
+  // those into LDS itself, so waiting for its own loads is all the synchronisation it
+  // needs.  One lane quantizes one whole block: no cross-lane step.
+  const int xt = tid - GW_STREAM;                                // 0 .. 511
+  const int xw = wave - 8;
+  const uint32_t bpr = (uint32_t)(K >> 4);                       // blocks per row
+  const uint32_t total = (uint32_t)M * bpr;
+  const int niter = (int)((total + GW_XT - 1) / GW_XT);
+  constexpr int BB = (T == InType::BF16) ? 32 : 64;              // bytes per block as stored
+  uint8_t* const xstage = (T == InType::BF16) ? gw_lds : sc_lds + gw_scale_bytes(K);
+  const int64_t sstride = (T == InType::BF16) ? TS : K * 4;      // staging bytes per token row
+  // row and block column of this wave's first block of step i (wave-uniform: the
+  // division runs on the scalar unit)
+  auto wave_block = [&](int i, uint32_t& row, uint32_t& bc) {
+    const uint32_t b0 = __builtin_amdgcn_readfirstlane((uint32_t)i * GW_XT + 64u * (uint32_t)xw);
+    row = b0 / bpr;
+    bc = b0 - row * bpr;
+  };
+  auto wave_has = [&](int i) { return (uint32_t)i * GW_XT + 64u * (uint32_t)xw < total; };
+  for (int i = 0; i < niter; ++i) {
+    if (wave_has(i)) {
+      uint32_t row, bc;
+      wave_block(i, row, bc);
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(p.x) + ((int64_t)row * p.ldx + bc * 16u) * (BB / 16);
+      uint8_t* dst = xstage + (int64_t)row * sstride + (int64_t)bc * BB;
+#pragma unroll
+      for (int h = 0; h < BB / 16; ++h)
+        __builtin_amdgcn_global_load_lds(src + 1024 * h + 16 * lane, dst + 1024 * h, 16, 0, 0);
+    }
+  }
+  // the weight scales (64 contiguous rows of K/16 bytes): 16-byte units
+  // u = j * 512 + xt at LDS offset 16 u; units past the last row clamp their source
+  // (in bounds; those rows are never stored)
+  {
+    const int64_t last = (min<int64_t>(N, n0 + GS_ROWS) - n0) * kb - 16;
+    const int nj = (int)((K + 2047) / 2048);
+    for (int j = 0; j < nj; ++j) {
+      const int64_t u = (int64_t)j * GW_XT + xt;
+      __builtin_amdgcn_global_load_lds(a.w_scales + n0 * kb + min<int64_t>(16 * u, last),
+                                       sc_lds + j * 8192 + xw * 1024, 16, 0, 0);
+    }
+  }
+  // Both issued before the stream: once the stream waves issue their loads, a load
+  // issued here would wait in the same queue behind them.
+  lds_sync();                                                    // barrier X: the stream starts now
+  wait_vmcnt<0>();                                               // this wave's x and scales are in LDS
+
+  // this lane's block of step i: staging offset, f16 offset, row, block column
+  auto lane_block = [&](int i, int64_t& soff, int64_t& xoff, uint32_t& row, uint32_t& bc) {
+    wave_block(i, row, bc);
+    bc += (uint32_t)lane;
+    soff = (int64_t)row * sstride + (int64_t)bc * BB;
+    xoff = (int64_t)row * TS + (int64_t)bc * 32;
+  };
+  auto load_block = [&](int64_t soff, float v[16]) {
+    const uint8_t* sp = xstage + soff;
+    if constexpr (T == InType::BF16) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const u32x4 q4 = *reinterpret_cast<const u32x4*>(sp + 16 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[8 * hh + 2 * e] = __uint_as_float(q4[e] << 16);
+          v[8 * hh + 2 * e + 1] = __uint_as_float(q4[e] & 0xFFFF0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const f32x4 f = *reinterpret_cast<const f32x4*>(sp + 16 * qq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * qq + e] = f[e];
+      }
+    }
+  };
+  float g = g_in;
+  if (dynamic) {
+    float am = 0.0f;
+    for (int i = 0; i < niter; ++i) {
+      if (wave_has(i)) {
+        int64_t soff, xoff;
+        uint32_t row, bc;
+        lane_block(i, soff, xoff, row, bc);
+        float v[16];
+        load_block(soff, v);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(v[e]));
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) am = __builtin_fmaxf(am, __shfl_xor(am, off));
+    if (lane == 0) red_g[xw] = am;
+    lds_sync();                                                  // barrier A
+    am = red_g[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) am = __builtin_fmaxf(am, red_g[i]);
+    g = global_scale_from_amax(am);
+  }
+  const ScaleConsts sc = scale_consts(g);
+  const bool codes_out = (blockIdx.x == 0) && (p.a_codes_out != nullptr);
+#pragma unroll 1
+  for (int i = 0; i < niter; ++i) {
+    if (wave_has(i)) {
+      int64_t soff, xoff;
+      uint32_t row, bc;
+      lane_block(i, soff, xoff, row, bc);
+      float xv[16];
+      load_block(soff, xv);
+      float am = __builtin_fabsf(xv[0]);
+#pragma unroll
+      for (int e = 1; e < 16; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(xv[e]));
+      const uint32_t sb = block_scale_byte(am, sc);
+      uint32_t w[2];
+      quant16(xv, sb, g, w);
+      const f16x2 s2 = scale_f16x2(sb);
+      *reinterpret_cast<f16x8*>(gw_lds + xoff) = decode8_f16(w[0], s2);
+      *reinterpret_cast<f16x8*>(gw_lds + xoff + 16) = decode8_f16(w[1], s2);
+      if (codes_out) {
+        *reinterpret_cast<u32x2*>(p.a_codes_out + (int64_t)row * (K >> 1) + bc * 8u) = u32x2{w[0], w[1]};
+        p.a_scales_out[(int64_t)row * (K >> 4) + bc] = (uint8_t)sb;
+      }
+    }
+  }
+  if (blockIdx.x == 0 && xt == 0 && p.gscale_out) *p.gscale_out = g;
+  lds_sync();                                                    // barrier B
+  __syncthreads();                                               // barrier C
 }
 
 }  // namespace
@@ -408,6 +670,32 @@ static hipError_t launch_stream(const GemvArgs& p, unsigned grid, size_t lds, hi
   return hipGetLastError();
 }
 
+// Code loads each stream wave of k_gemv_ws keeps in flight (issued before the x
+// barrier, then one per step).  Measured at 4 x 16384 x 5120: 10-14 of 20 are within
+// noise of each other; 8 and 20 are slower.
+#ifndef NVFP4_GEMV_WS_AHEAD
+#define NVFP4_GEMV_WS_AHEAD(nl) ((nl) / 2)
+#endif
+
+template <InType T, int NL>
+static hipError_t launch_ws(const GemvArgs& p, unsigned grid, size_t lds, hipStream_t s) {
+  constexpr int NA = NVFP4_GEMV_WS_AHEAD(NL);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ws<T, NL, NA>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, GW_LDS_MAX);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((k_gemv_ws<T, NL, NA>), dim3(grid), dim3(GW_THREADS), lds, s, p);
+  return hipGetLastError();
+}
+
+static bool gemv_ws_fits(int64_t M, int64_t K, InType t) {
+  return M <= 8 && K % 1024 == 0 && K / 256 <= GS_NLMAX &&
+         gw_lds_bytes(M, K, t == InType::F32) <= GW_LDS_MAX;
+}
+
 bool gemv_stream_fits(int64_t M, int64_t K, InType t) {
   const int64_t chunks_per_thread = (M * K / 8 + GS_THREADS - 1) / GS_THREADS;
   return M <= 8 && K % 512 == 0 && K >= 512 && K / 256 <= GS_NLMAX && chunks_per_thread <= GS_XMAX &&
@@ -415,6 +703,20 @@ bool gemv_stream_fits(int64_t M, int64_t K, InType t) {
 }
 
 hipError_t launch_gemv_fused(const GemvArgs& p, hipStream_t s) {
+  if (gemv_ws_fits(p.g.M, p.g.K, p.x_type)) {
+    const unsigned grid = (unsigned)((p.g.N + GS_ROWS - 1) / GS_ROWS);
+    const size_t lds = (size_t)gw_lds_bytes(p.g.M, p.g.K, p.x_type == InType::F32);
+    switch ((int)(p.g.K / 256)) {
+#define NVFP4_GW_CASE(nl)                                                                  \
+  case nl:                                                                                 \
+    return p.x_type == InType::BF16 ? launch_ws<InType::BF16, nl>(p, grid, lds, s)        \
+                                    : launch_ws<InType::F32, nl>(p, grid, lds, s);
+      NVFP4_GW_CASE(4) NVFP4_GW_CASE(8) NVFP4_GW_CASE(12) NVFP4_GW_CASE(16)        // K % 1024 == 0
+      NVFP4_GW_CASE(20) NVFP4_GW_CASE(24) NVFP4_GW_CASE(28) NVFP4_GW_CASE(32)
+#undef NVFP4_GW_CASE
+      default: break;
+    }
+  }
   if (gemv_stream_fits(p.g.M, p.g.K, p.x_type)) {
     const unsigned grid = (unsigned)((p.g.N + GS_ROWS - 1) / GS_ROWS);
     const size_t lds = (size_t)gs_lds_bytes(p.g.M, p.g.K);

@@ -36,6 +36,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // E4M3 (OCP FN) byte -> fp32.  gfx950's fp8 conversion implements OCP E4M3FN.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {

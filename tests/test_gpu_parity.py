@@ -440,6 +440,25 @@ def test_linear_skinny_fused(nv, M, N, seg_end, K, xdt, gate_heads, y_dtype, mod
     """The fused skinny-N linear (x read once, quantized in registers) against the
     oracle: global scale and (when requested) codes bit-exact, outputs within the
     GEMM tolerance."""
+    _check_linear(nv, M, N, seg_end, K, xdt, gate_heads, y_dtype, mode, codes_out, "skinny")
+
+
+@pytest.mark.parametrize("M,N,seg_end,K,xdt,gate_heads,y_dtype", [
+    (4, 96, [48, 96], 5120, "bf16", 48, "f32"),        # decode GEMV with the gate epilogue
+    (1, 1000, [300, 1000], 2048, "f32", 0, "f32"),     # one token, fp32 in and out, ragged N
+    (8, 520, [256, 520], 1024, "bf16", 0, "bf16"),     # eight tokens, ragged last workgroup
+    (3, 200, [200], 1536, "bf16", 0, "bf16"),          # K % 1024 != 0: the other decode kernel
+])
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("codes_out", [True, False])
+def test_linear_decode_fused(nv, M, N, seg_end, K, xdt, gate_heads, y_dtype, mode, codes_out):
+    """The fused decode GEMV (M <= 8) through nvfp4_w4a4_linear against the oracle:
+    global scale and (when requested) codes bit-exact, outputs within the GEMM
+    tolerance."""
+    _check_linear(nv, M, N, seg_end, K, xdt, gate_heads, y_dtype, mode, codes_out, "decode")
+
+
+def _check_linear(nv, M, N, seg_end, K, xdt, gate_heads, y_dtype, mode, codes_out, what):
     wl = _skinny_case(M, N, seg_end, K, xdt, seed=M * 31 + N * 7 + K, gate_heads=gate_heads, y_dtype=y_dtype)
     act = 0.0457 if mode == "static" else None
     xv, xt = _x_inputs(wl)
@@ -464,7 +483,7 @@ def test_linear_skinny_fused(nv, M, N, seg_end, K, xdt, gate_heads, y_dtype, mod
         P.assert_bytes_equal(as_.cpu().numpy(), os_, "activation scales")
     ogate = (wl.data["A_log"], wl.data["dt_bias"]) if gate_heads else None
     yref, _, bound = P.oracle_reference(oc, os_, og, owc, ows, wl.seg_end, owg, y_dtype, gate=ogate)
-    P.assert_within_tolerance(P.y_to_f64(y), yref, bound, f"skinny M={M} N={N} K={K} {xdt} {mode}")
+    P.assert_within_tolerance(P.y_to_f64(y), yref, bound, f"{what} M={M} N={N} K={K} {xdt} {mode}")
 
 
 def test_linear_skinny_equals_two_stage(nv):
