@@ -16,14 +16,14 @@
 //    the subnormal range).  Subnormal scales and extreme global scales take one
 //    float64 division instead (exact there: midpoints have <= 5 significant bits, a
 //    non-zero gap is >= ~2^-32 relative, the division error <= 2^-53).
-//  * Codes: y = x * rcp(s g) in fp32 (|y - r| <= 3 ulp(y)) converted by the hardware
-//    E2M1 RNE conversion (v_cvt_scalef32_pk_fp4_f32: exact RNE with saturation at 6,
-//    the sign of x kept, power-of-two scale 1.0).  A code can only be wrong if a
-//    midpoint lies within that distance; every midpoint has <= 3 significant bits (its
-//    low 21 mantissa bits are zero), and for a y within 16 ulps of such a value v the
-//    sign of |x| - v s g, again one exactly-signed fma (v s has <= 7 significant bits),
-//    picks the code.  Blocks whose s g is outside [2^-100, 2^120] are redone in float64
-//    (the product s g is exact there).
+//  * Codes: two fp32 quotients lo = |x| rcp(s g) (1 - 2^-19) and hi = |x| rcp(s g)
+//    (1 + 2^-19) bracket the exact q = |x| / (s g) strictly; both go through the
+//    hardware E2M1 RNE conversion (v_cvt_scalef32_pk_fp4_f32: exact RNE with
+//    saturation at 6, the sign of the input kept, power-of-two scale 1.0).  Equal codes
+//    are the code of q.  Different codes mean that a midpoint m lies inside the
+//    bracket, and the sign of |x| - m s g, again one exactly-signed fma (m s has <= 7
+//    significant bits), picks the code.  Blocks whose s g is outside [2^-100, 2^120]
+//    are redone in float64 (the product s g is exact there).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -136,71 +136,70 @@ __device__ __forceinline__ uint32_t e2m1_code_exact(float x, double h) {
   return c | ((__float_as_uint(x) >> 28) & 8u);
 }
 
-// Per-block constants of the code computation: y = x * rh with rh = rcp(s g).
+// Per-block constants of the code computation.  rl and rh bracket 1 / (s g):
+// rl = rcp(s g) (1 - 2^-19) and rh = rcp(s g) (1 + 2^-19), each rounded once, so that
+// for every x, fl(|x| rl) < |x| / (s g) < fl(|x| rh) (the rounding of s g, of rcp
+// (<= 1 ulp) and of the two products add up to less than 5 * 2^-24 relative).
 struct BlockConsts {
   float s;        // decoded block scale
-  float rh;       // rcp(s g) (<= 1 ulp), 0 for a zero block: codes keep only the sign
-  bool zero;      // block scale 0 or global scale 0: magnitude codes 0
-  bool fast_ok;   // s g in [2^-100, 2^120]: 1/(s g) is normal and the exact-sign fma
-                  // of e2m1_code_near stays clear of the subnormal range
+  float s4;       // s / 4 (exact)
+  float rl, rh;   // the bracket; 0 for a zero block: codes keep only the sign
+  bool fast_ok;   // zero block, or s g in [2^-100, 2^120]: 1/(s g) is normal and the
+                  // exact-sign fma below stays clear of the subnormal range
 };
 
 __device__ __forceinline__ BlockConsts block_consts(uint32_t sb, float g) {
   BlockConsts b;
   b.s = e4m3_to_f32(sb);
+  b.s4 = 0.25f * b.s;
   const float h32 = b.s * g;
-  b.zero = (sb == 0u) || !(g > 0.0f);
-  b.fast_ok = b.zero || (h32 >= 0x1p-100f && h32 <= 0x1p120f);
-  b.rh = b.zero ? 0.0f : __builtin_amdgcn_rcpf(h32);
+  const bool zero = (sb == 0u) || !(g > 0.0f);
+  b.fast_ok = zero || (h32 >= 0x1p-100f && h32 <= 0x1p120f);
+  const float r = zero ? 0.0f : __builtin_amdgcn_rcpf(h32);
+  b.rl = r * (1.0f - 0x1p-19f);
+  b.rh = r * (1.0f + 0x1p-19f);
   return b;
 }
 
-// key(y) = low 21 mantissa bits of y + 16, moved to the top: < 33 << 11 iff y is
-// within 16 ulps of a value whose low 21 mantissa bits are zero (every E2M1 midpoint)
-__device__ __forceinline__ uint32_t near_key(float y) { return (__float_as_uint(y) << 11) + (16u << 11); }
-
-// Exact E2M1 code of x whose fast quotient y = x * rcp(s g) lies within 16 ulps of a
-// value v with <= 3 significant bits (every E2M1 midpoint is one).  The exact
-// quotient q = |x| / (s g) is within ~20 ulps of v, so its code is one of the codes
-// on either side of v: those of v (1 -/+ 2^-11), found with one packed conversion
-// (equal unless v is a midpoint).  The sign of |x| - v s g, from one fma (v s has
-// <= 7 significant bits, so v s * g + |x| is rounded once and keeps its sign),
-// picks between them; an exact tie goes to the even code.  Requires s g normal.
-__device__ __forceinline__ uint32_t e2m1_code_near(float x, float y, float s, float g) {
-  const float ax = __builtin_fabsf(x);
-  const float v = __uint_as_float((__float_as_uint(__builtin_fabsf(y)) + 0x100000u) & 0xFFE00000u);
-  const uint32_t cc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v * 0.99951171875f, v * 1.00048828125f, 1.0f, 0);
-  const uint32_t down = cc & 7u, up = (cc >> 4) & 7u;
-  const float r = __builtin_fmaf(-(v * s), g, ax);
-  const uint32_t mag = (r > 0.0f) ? up : ((r < 0.0f) ? down : ((down & 1u) ? up : down));
-  return mag | ((__float_as_uint(x) >> 28) & 8u);
+// 8 values -> 8 E2M1 codes by the hardware RNE conversion (element 0 in the low
+// nibble; saturation at 6, the sign of each value kept)
+__device__ __forceinline__ uint32_t cvt8_fp4(const float* y) {
+  uint32_t x = 0;
+  x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[0], y[1], 1.0f, 0);
+  x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[2], y[3], 1.0f, 1);
+  x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[4], y[5], 1.0f, 2);
+  x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[6], y[7], 1.0f, 3);
+  return x;
 }
 
 // Codes of n consecutive values v[0..n) of one block (n = 8 or 16) into w[n/8]
-// (element 0 in the low nibble of w[0]).  Elements whose fast quotient is within 16
-// ulps of a <= 3-significant-bit value are decided exactly, one by one
-// (e2m1_code_near); the float64 recomputation of the whole block is left for blocks
-// whose s g or 1/(s g) is not a normal fp32 value (extreme scales).  The empty asm
-// makes s opaque there, so the compiler cannot hoist the float64 product into the
-// common path.
+// (element 0 in the low nibble of w[0]).  The codes of the bracket ends lo = |x| rl
+// and hi = |x| rh are computed for every element; where they agree, every value in
+// between, the exact quotient q = |x| / (s g) included, has that code (RNE is
+// monotone).  Where they differ, the bracket (2^-18 wide, relative) holds exactly one
+// E2M1 midpoint m, between the codes dn and dn + 1: the sign of |x| - m s g, from one
+// fma (m s has <= 7 significant bits, so -(m s) is exact and m s * g + |x| is rounded
+// once and keeps its sign), says on which side q lies; an exact tie goes to the even
+// code.  Such elements are handled per element position with a wave-uniform test, the
+// decision taken branch-free for all lanes.  Blocks whose s g or 1/(s g) is not a
+// normal fp32 value (extreme scales) are recomputed in float64; the empty asm makes
+// s opaque there, so the compiler cannot hoist the float64 product into the common
+// path.
 template <int NV>
 __device__ __forceinline__ void quant_block(const float v[NV], const BlockConsts& b, float g, uint32_t w[NV / 8]) {
-  float y[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) y[i] = v[i] * b.rh;
+  uint32_t diff = 0, wh[NV / 8];
 #pragma unroll
   for (int d = 0; d < NV / 8; ++d) {
-    uint32_t x = 0;
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * d + 0], y[8 * d + 1], 1.0f, 0);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * d + 2], y[8 * d + 3], 1.0f, 1);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * d + 4], y[8 * d + 5], 1.0f, 2);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * d + 6], y[8 * d + 7], 1.0f, 3);
-    w[d] = x;
-  }
-  uint32_t k = 0xFFFFFFFFu;
+    float lo[8], hi[8];
 #pragma unroll
-  for (int i = 0; i < NV; i += 2) k = min(k, min(near_key(y[i]), near_key(y[i + 1])));
-  if (b.zero) return;
+    for (int e = 0; e < 8; ++e) {
+      lo[e] = v[8 * d + e] * b.rl;
+      hi[e] = v[8 * d + e] * b.rh;
+    }
+    w[d] = cvt8_fp4(lo);
+    wh[d] = cvt8_fp4(hi);
+    diff |= w[d] ^ wh[d];
+  }
   if (!b.fast_ok) {
     float sv = b.s;
     asm volatile("" : "+v"(sv));
@@ -210,13 +209,17 @@ __device__ __forceinline__ void quant_block(const float v[NV], const BlockConsts
       const uint32_t c = e2m1_code_exact(v[i], h);
       w[i / 8] = (w[i / 8] & ~(0xFu << (4 * (i % 8)))) | (c << (4 * (i % 8)));
     }
-  } else if (k < (33u << 11)) {
+  } else if (__builtin_amdgcn_ballot_w64(diff != 0u) != 0u) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      // |y| >= 8: saturated at 6, no midpoint near (also keeps inf out of the exact path)
-      if (near_key(y[i]) < (33u << 11) && __builtin_fabsf(y[i]) < 8.0f) {
-        const uint32_t c = e2m1_code_near(v[i], y[i], b.s, g);
-        w[i / 8] = (w[i / 8] & ~(0xFu << (4 * (i % 8)))) | (c << (4 * (i % 8)));
+      const int d = i / 8, sh = 4 * (i % 8);
+      const uint32_t dn = (w[d] >> sh) & 7u, up = (wh[d] >> sh) & 7u;
+      if (__builtin_amdgcn_ballot_w64(dn != up) != 0u) {
+        // midpoint between codes dn and dn + 1, times 4: 1 3 5 7 10 14 20 (dn = 0 .. 6)
+        const uint32_t m4 = __builtin_amdgcn_perm(0x00140E0Au, 0x07050301u, dn) & 0xFFu;
+        const float r = __builtin_fmaf(-((float)m4 * b.s4), g, __builtin_fabsf(v[i]));
+        const uint32_t take_up = ((uint32_t)(r > 0.0f) | ((uint32_t)(r == 0.0f) & dn)) & 1u;
+        w[d] += ((dn != up) && take_up ? (up - dn) : 0u) << sh;
       }
     }
   }
