@@ -214,6 +214,14 @@ __device__ __forceinline__ void big_tile_of(int64_t M, int64_t N, int64_t pid, i
   *bm = first_m + (logical % per_group) % gsize;
   *bn = (logical % per_group) / gsize;
 }
+// Direct-to-LDS buffer loads: lane l lands at lds + size * l (the LDS address
+// is wave-uniform, set in M0); vector offset per lane, scalar offset per wave.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
+}
 constexpr int GST = 4;                                  // LDS stages
 constexpr int ST_A = 0, ST_W = 8192, ST_SA = 16384, ST_SW = 17408, ST_BYTES = 18432;
 
@@ -223,7 +231,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform values through readfirstlane: the compiler keeps what derives from
+  // them (LDS bases, M0) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, li = lane & 31;
 
@@ -240,8 +250,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   // 2j and 2j+1 fetch the two halves of one row: 32 contiguous bytes), 64 rows of A
   // and of W scales.  Rows past M or N are clamped to the last row (in bounds; their
   // outputs are never stored).
-  const uint8_t* ga_c[2];
-  const uint8_t* gw_c[2];
+  // Global addresses: a uniform base that advances with k (scalar registers) plus a
+  // fixed 32-bit offset per lane (each packed operand is < 2^31 bytes, checked on the
+  // host), so a load costs no vector address arithmetic.
+  uint32_t oa_c[2], ow_c[2];
   uint32_t lo_c[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -250,39 +262,59 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
     const int hl = (lane & 1) ^ (((row >> 2) ^ (row >> 3)) & 1);      // logical half of this slot
     const int64_t ra = min<int64_t>(m0 + row, a.M - 1);
     const int64_t rw = min<int64_t>(n0 + row, a.N - 1);
-    ga_c[q] = a.a_codes + ra * kh + 16 * hl;
-    gw_c[q] = a.w_codes + rw * kh + 16 * hl;
+    oa_c[q] = (uint32_t)(ra * kh + 16 * hl);
+    ow_c[q] = (uint32_t)(rw * kh + 16 * hl);
     lo_c[q] = (uint32_t)(r0 * 32);
   }
-  const uint8_t* ga_s = a.a_scales + min<int64_t>(m0 + 64 * wave + lane, a.M - 1) * kb;
-  const uint8_t* gw_s = a.w_scales + min<int64_t>(n0 + 64 * wave + lane, a.N - 1) * kb;
+  const uint32_t oa_s = (uint32_t)(min<int64_t>(m0 + 64 * wave + lane, a.M - 1) * kb);
+  const uint32_t ow_s = (uint32_t)(min<int64_t>(n0 + 64 * wave + lane, a.N - 1) * kb);
   const uint32_t lo_s = (uint32_t)(64 * wave * 4);
+  // buffer descriptors of the four packed operands (size = byte extent)
+  const __amdgpu_buffer_rsrc_t ra_c = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.a_codes), (short)0,
+                                                                        (int)(a.M * kh), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw_c = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.w_codes), (short)0,
+                                                                        (int)(a.N * kh), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra_s = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.a_scales), (short)0,
+                                                                        (int)(a.M * kb), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw_s = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.w_scales), (short)0,
+                                                                        (int)(a.N * kb), 0x00020000);
   auto issue = [&](int st, int64_t k0) {
     uint8_t* base = smem + st * ST_BYTES;
+    const int kc = (int)(k0 >> 1), ks = (int)(k0 >> 4);          // wave-uniform offsets
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      __builtin_amdgcn_global_load_lds(ga_c[q] + (k0 >> 1), base + ST_A + lo_c[q], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(gw_c[q] + (k0 >> 1), base + ST_W + lo_c[q], 16, 0, 0);
+      buffer_load_lds16(ra_c, base + ST_A + lo_c[q], oa_c[q], kc);
+      buffer_load_lds16(rw_c, base + ST_W + lo_c[q], ow_c[q], kc);
     }
-    __builtin_amdgcn_global_load_lds(ga_s + (k0 >> 4), base + ST_SA + lo_s, 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(gw_s + (k0 >> 4), base + ST_SW + lo_s, 4, 0, 0);
+    buffer_load_lds4(ra_s, base + ST_SA + lo_s, oa_s, ks);
+    buffer_load_lds4(rw_s, base + ST_SW + lo_s, ow_s, ks);
   };
 
+  // LDS read addresses: a per-lane base (computed once) plus the stage offset; the row
+  // block i adds an immediate.  Row r = w*128 + i*32 + li: bits 2 and 3 of r (the
+  // half swap) are those of li.
+  const int swz = (li >> 2 ^ li >> 3) & 1;
+  const uint32_t la_c = (uint32_t)(ST_A + (wm * 128 + li) * 32 + 16 * (h ^ swz));
+  const uint32_t lw_c = (uint32_t)(ST_W + (wn * 128 + li) * 32 + 16 * (h ^ swz));
+  const uint32_t la_s = (uint32_t)(ST_SA + (wm * 128 + li) * 4 + 2 * h);
+  const uint32_t lw_s = (uint32_t)(ST_SW + (wn * 128 + li) * 4 + 2 * h);
   u32x4 ca[4], cw[4];          // packed codes of this lane's rows for the current K step
   f16x2 pa[4], pw[4];          // scale pairs {block 2h, block 2h+1}
   auto lread = [&](int st) {
     const uint8_t* base = smem + st * ST_BYTES;
+    const uint8_t* pac = base + la_c;
+    const uint8_t* pwc = base + lw_c;
+    const uint8_t* pas = base + la_s;
+    const uint8_t* pws = base + lw_s;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = wm * 128 + i * 32 + li;
-      ca[i] = *reinterpret_cast<const u32x4*>(base + ST_A + r * 32 + 16 * (h ^ (((r >> 2) ^ (r >> 3)) & 1)));
-      pa[i] = scale_pair_f16(*reinterpret_cast<const uint16_t*>(base + ST_SA + r * 4 + 2 * h));
+      ca[i] = *reinterpret_cast<const u32x4*>(pac + i * 1024);
+      pa[i] = scale_pair_f16(*reinterpret_cast<const uint16_t*>(pas + i * 128));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = wn * 128 + j * 32 + li;
-      cw[j] = *reinterpret_cast<const u32x4*>(base + ST_W + r * 32 + 16 * (h ^ (((r >> 2) ^ (r >> 3)) & 1)));
-      pw[j] = scale_pair_f16(*reinterpret_cast<const uint16_t*>(base + ST_SW + r * 4 + 2 * h));
+      cw[j] = *reinterpret_cast<const u32x4*>(pwc + j * 1024);
+      pw[j] = scale_pair_f16(*reinterpret_cast<const uint16_t*>(pws + j * 128));
     }
   };
   f16x8 A0[4], B0[4], A1[4], B1[4];
@@ -446,7 +478,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
 
 template <int EPI>
 static hipError_t launch_gemm_epi(const GemmArgs& a, hipStream_t s) {
-  if (EPI != EPI_GATE && a.K % GBK == 0 && a.K >= 3 * GBK && a.M >= 512 && a.N >= 512) {
+  // k_gemm_big addresses each packed operand with 32-bit offsets
+  const bool offsets32 = a.M * (a.K / 2) < (int64_t(1) << 31) && a.N * (a.K / 2) < (int64_t(1) << 31);
+  if (EPI != EPI_GATE && a.K % GBK == 0 && a.K >= 3 * GBK && a.M >= 512 && a.N >= 512 && offsets32) {
     const int64_t big_tiles = ((a.M + GBM - 1) / GBM) * ((a.N + GBN - 1) / GBN);
     if constexpr (EPI != EPI_GATE) {
       hipLaunchKernelGGL(k_gemm_big<EPI>, dim3((unsigned)big_tiles), dim3(256), 0, s, a);
