@@ -79,6 +79,33 @@ def setup_layer(nv, wl, seg_gscale=None):
     return xt, wc, ws, wg
 
 
+def timed_steps(step, steps):
+    """Wall time per step (ms) of exactly `steps` back-to-back steps, bracketed by
+    device synchronizations; nothing but the steps' own launches is enqueued."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def event_breakdown(step, steps):
+    """Mean HIP-event durations (ms) of the two launches of a step, measured in a
+    separate pass after the timed one (event records between launches would add
+    their own gaps to the timed steps)."""
+    import torch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    first = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    second = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    return first, second
+
+
 def time_prefill(nv, xt, wc, ws, wg, seg_end, steps, warmup, static_g, y_dtype):
     """Time `steps` steps of quantize + GEMM.  Returns wall ms/step and the mean
     HIP-event durations of the quantize (and amax) part and of the GEMM launch."""
@@ -103,15 +130,8 @@ def time_prefill(nv, xt, wc, ws, wg, seg_end, steps, warmup, static_g, y_dtype):
 
     for _ in range(warmup):
         step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    wall = timed_steps(step, steps)
+    q_ms, g_ms = event_breakdown(step, steps)
     return wall, q_ms, g_ms, y
 
 
@@ -211,15 +231,8 @@ def time_config(nv, name, steps, warmup):
 
     for _ in range(warmup):
         step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    wall = timed_steps(step, steps)
+    q_ms, g_ms = event_breakdown(step, steps)
     flops = 2.0 * M * N * K
     ybytes = M * N * (2 if wl.y_dtype == "bf16" else 4)
     packed = lambda rows: rows * K // 2 + rows * K // 16
@@ -322,8 +335,8 @@ def cpu_baseline(wl, static_g, target_s=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dynamic", action="store_true")
