@@ -6,7 +6,7 @@ current HIP stream.  The functions carry the C names and raise Nvfp4Error with t
 library's message when a call returns an error status.
 
 Importing this package loads the library and raises ImportError if it has not
-been built (``python -m nvfp4_w4a4_quantized_amd.build``); there is no fallback.
+been built (``python nvfp4_w4a4_quantized_amd/build.py``); there is no fallback.
 """
 
 from __future__ import annotations
@@ -43,7 +43,7 @@ class GateParams(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run `python -m nvfp4_w4a4_quantized_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built: run `python nvfp4_w4a4_quantized_amd/build.py` "
                           "(the NVFP4 layer has no non-HIP implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64

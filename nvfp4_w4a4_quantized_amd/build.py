@@ -3,7 +3,9 @@
 Each source is compiled to an object in its own process (in parallel), then the
 objects are linked into the shared library.  Every call rebuilds everything.
 
-    python -m nvfp4_w4a4_quantized_amd.build
+    python nvfp4_w4a4_quantized_amd/build.py
+
+It imports nothing from the package, whose import needs the built library.
 """
 
 import os
