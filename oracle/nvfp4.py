@@ -394,3 +394,45 @@ def gate_elem_bound(y64_gemm, gemm_bound, A_log, dt_bias, out_rounded):
         + 8 * U32 * np.abs(g) + ulp(out_rounded[:, :H], "f32")
     bb = beta * (1 - beta) * gemm_bound[:, H:] + 8 * U32 * beta + ulp(out_rounded[:, H:], "f32")
     return np.concatenate([bg, bb], axis=1)
+
+
+# ----------------------------------------------------------------------------
+# Harmonization onto one shared global scale, and the mismatch factor
+# ----------------------------------------------------------------------------
+
+def requantize_shared_scale(codes, scales, seg_end, g_seg, g_shared=None):
+    """Re-encode a weight packed with one global scale per fused-output segment
+    onto one global scale for the whole fused weight: the alternative repair of
+    the fused-GEMM global-scale mismatch, where the per-segment epilogue is the
+    other [GDN-4bit review, strengths paragraph (the paper's section 6);
+    GDN-4bit abstract].
+
+    Reading (the pages name the mismatch and its repair, not a re-encoding
+    recipe): every row is dequantized exactly with its own segment's scale,
+    x_hat = e2m1 * s * g_seg[seg(row)], and quantized again with the shared
+    scale by the same steps as any NVFP4 tensor (quantize_rows).  g_shared
+    defaults to the largest segment scale, so no block scale needs more range
+    than it had.  float64 stays exact: x_hat has <= 2 + 4 + 24 significant bits,
+    compared with midpoints times <= 31-bit values (see the module docstring).
+
+    Returns (codes', scales', g_shared float32)."""
+    g_seg = np.asarray(g_seg, dtype=np.float32)
+    N = np.asarray(codes).shape[0]
+    seg = segment_rows(seg_end, N)
+    x_hat = dequantize_rows(codes, scales, g_seg[seg])
+    gs = np.float32(np.max(g_seg)) if g_shared is None else np.float32(g_shared)
+    c2, s2 = quantize_rows(x_hat, np.full(N, gs, dtype=np.float32))
+    return c2, s2, gs
+
+
+def segment_mismatch_factor(g_seg, g_used):
+    """Factor by which a fused GEMM that applies the one global scale g_used to
+    every segment mis-scales the worst segment's outputs: max over segments of
+    max(g_used / g_s, g_s / g_used) (1.0 when every segment has scale g_used);
+    also returns that segment's index.  [GDN-4bit review, strengths paragraph:
+    the mismatch is silent, so it has to be detected]"""
+    g = np.asarray(g_seg, dtype=np.float32).astype(np.float64)
+    u = float(np.float32(g_used))
+    f = np.maximum(u / g, g / u)
+    worst = int(np.argmax(f))
+    return float(f[worst]), worst

@@ -404,3 +404,87 @@ def test_error_bound_admits_fp32_gemm_and_rejects_planted_error():
     planted = ygpu.copy()
     planted[3, 7] *= 1.01
     assert np.any(np.abs(planted - yref) > bound)
+
+
+# --------------------------------------------------------------------------- shared-scale re-encoding
+
+def _xhat_rows(codes, scales, g_rows):
+    """Exact dequantized values (Python floats: <= 30 significant bits) from the
+    golden E2M1 table and torch's E4M3 values, independent of the oracle."""
+    rows = []
+    for r in range(codes.shape[0]):
+        g = float(np.float32(g_rows[r]))
+        row = []
+        for j, byte in enumerate(codes[r]):
+            for c in (int(byte) & 15, int(byte) >> 4):
+                k = len(row)
+                s = float(E4M3_TORCH[int(scales[r, k // 16])])
+                v = E2M1_GOLDEN[c] * s * g
+                row.append(math.copysign(abs(v), -1.0) if c & 8 else v)
+        rows.append(row)
+    return rows
+
+
+def test_requantize_shared_scale_brute_force():
+    """Bytes of the re-encoding equal exhaustive rational quantization of the exact
+    dequantized values under the shared scale (subnormal block scales included)."""
+    rng = np.random.default_rng(21)
+    seg_end = [3, 5, 8]
+    w = rng.standard_normal((8, 64)) * np.repeat([0.02, 0.3, 0.005], [3, 2, 3])[:, None]
+    w[1, 16:32] *= 1e-3                                    # blocks with subnormal scales
+    w[6, 0:16] = 0.0                                       # a zero block
+    w[6, 0] = -0.0
+    w64 = w.astype(np.float32).astype(np.float64)
+    c, s, g = O.pack_weight(w64, seg_end)
+    seg = O.segment_rows(seg_end, 8)
+    assert len(set(g.tolist())) == 3
+    for g_shared in (None, np.float32(g.max() * np.float32(1.7))):
+        c2, s2, gs = O.requantize_shared_scale(c, s, seg_end, g, g_shared)
+        assert gs == (g.max() if g_shared is None else g_shared)
+        bc, bs = brute_quantize(_xhat_rows(c, s, g[seg]), gs)
+        assert np.array_equal(c2, bc) and np.array_equal(s2, bs)
+
+
+def test_requantize_identity_and_power_of_two_shift():
+    """Same scale: the re-encoding is the identity on normal-scale blocks (their
+    largest element has code 6, so amax = 6 s g).  Shared scale 2^k g_s: codes
+    unchanged and every scale byte lowered by 8k (exponent field - k) while the
+    shifted scale stays normal."""
+    rng = np.random.default_rng(22)
+    w64 = (rng.standard_normal((16, 256)) * 0.05).astype(np.float32).astype(np.float64)
+    c, s, g = O.pack_weight(w64, [16])
+    assert s.min() >= 8 + 16                               # normal, and still normal after -16
+    c1, s1, g1 = O.requantize_shared_scale(c, s, [16], g)
+    assert g1 == g[0] and np.array_equal(c1, c) and np.array_equal(s1, s)
+    c2, s2, g2 = O.requantize_shared_scale(c, s, [16], g, g[0] * np.float32(4))
+    assert np.array_equal(c2, c) and np.array_equal(s2.astype(int), s.astype(int) - 16)
+
+
+def test_requantize_keeps_codes_and_rerounds_scales():
+    """Under a larger shared scale a normal-scale block keeps its codes and its
+    scale becomes E4M3-RNE(s g_s / g_shared): the block maximum (code 6) gives
+    t' = s g_s / g_shared exactly, and the re-rounded scale moves the element
+    quotients by at most 1/16, less than the 12.5 % to the nearest E2M1 midpoint."""
+    rng = np.random.default_rng(23)
+    seg_end = [32, 64]
+    w = rng.standard_normal((64, 128)) * np.repeat([0.02, 0.0826], 32)[:, None]
+    c, s, g = O.pack_weight(w.astype(np.float32).astype(np.float64), seg_end)
+    c2, s2, gs = O.requantize_shared_scale(c, s, seg_end, g)
+    assert gs == g[1] and 2.0 < g[1] / g[0] < 4.0        # not a power of two
+    assert s[:32].min() >= 8 + 24                          # scales stay normal after / 4
+    assert np.array_equal(c2, c)
+    assert np.array_equal(s2[32:], s[32:])
+    gF = [Fraction(float(v)) for v in g]
+    for r in range(32):
+        for b in range(s.shape[1]):
+            t = _E4M3_F[int(s[r, b])] * gF[0] / Fraction(float(gs))
+            assert s2[r, b] == _nearest_even(_E4M3_F, t)
+
+
+def test_segment_mismatch_factor():
+    g = np.array([1.5e-5, 6.0e-5], dtype=np.float32)      # up scale = 4 x gate scale
+    assert O.segment_mismatch_factor(g, g[0]) == (4.0, 1)
+    assert O.segment_mismatch_factor(g, g[1]) == (4.0, 0)
+    assert O.segment_mismatch_factor(np.full(3, g[0]), g[0]) == (1.0, 0)
+    f, worst = O.segment_mismatch_factor(np.array([1.0, 3.0, 0.25], dtype=np.float32), 1.0)
+    assert (f, worst) == (4.0, 2)
