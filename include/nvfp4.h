@@ -164,6 +164,46 @@ NVFP4_API int32_t nvfp4_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, i
                           void* y, int32_t y_dtype, int64_t ldy,
                           uint8_t* a_codes_out, uint8_t* a_scales_out, void* stream);
 
+/*
+ * Re-encoding of a fused weight onto one shared global scale: the alternative
+ * repair of the fused-GEMM global-scale mismatch, where the per-segment epilogue
+ * of nvfp4_w4a4_gemm is the other ("Why Gated DeltaNet Survives 4-Bit
+ * Quantization" review page, strengths paragraph / the paper's section 6).
+ * Every row is dequantized exactly with its segment's scale (e2m1 * s * g_seg)
+ * and quantized again, by the numerics above, under the shared scale.  The
+ * result is one NVFP4 tensor: a GEMM over it takes n_seg = 1 and the scale
+ * written to gscale_out.  Blocks whose scale stays in the normal E4M3 range
+ * keep their codes when the shared scale is the largest segment scale; their
+ * scale bytes are re-rounded, so the re-encoding can cost up to 1/16 relative
+ * per block (none when the scales differ by powers of two).
+ *   codes, scales  device, packed weight [N][K/2], [N][K/16] (as packed by
+ *                  nvfp4_pack_weight)
+ *   n_seg, seg_end host segment table over the N rows (as for nvfp4_pack_weight)
+ *   seg_gscale     device, n_seg fp32: the segment scales the weight was packed with
+ *   gscale_shared  device, 1 fp32 (finite, > 0), or NULL: the largest segment scale
+ *   codes_out, scales_out device outputs [N][K/2], [N][K/16]; may be the same
+ *                  buffers as codes, scales (in place), otherwise must not overlap them
+ *   gscale_out     device, 1 fp32 (output): the shared scale used
+ */
+NVFP4_API int32_t nvfp4_requantize_weight(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                                int32_t n_seg, const int64_t* seg_end, const float* seg_gscale,
+                                const float* gscale_shared, uint8_t* codes_out, uint8_t* scales_out,
+                                float* gscale_out, void* stream);
+
+/*
+ * Detector of the global-scale mismatch (host only, nothing enqueued): for a
+ * fused weight packed with the segment scales seg_gscale (host, n_seg fp32,
+ * finite, > 0), a GEMM that applied the single scale g_used (finite, > 0) to
+ * every segment would scale segment s's outputs by g_used / g_s.  Writes the
+ * worst factor max_s max(g_used / g_s, g_s / g_used) (1.0 = no mismatch) to
+ * *factor_out and that segment's index to *worst_out (either may be NULL).
+ * The mismatch is silent in the outputs (review page, strengths paragraph), so
+ * callers that fuse separately calibrated modules check this before launching a
+ * single-scale GEMM.
+ */
+NVFP4_API int32_t nvfp4_segment_mismatch_factor(int32_t n_seg, const float* seg_gscale, float g_used,
+                                      double* factor_out, int32_t* worst_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ NVFP4_DTYPE_BF16 = 1
 NVFP4_MAX_SEGMENTS = 64
 
 EXPORTED = ["nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize_act", "nvfp4_pack_weight",
-            "nvfp4_w4a4_gemm", "nvfp4_w4a4_linear"]
+            "nvfp4_w4a4_gemm", "nvfp4_w4a4_linear", "nvfp4_requantize_weight", "nvfp4_segment_mismatch_factor"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -59,6 +59,10 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_w4a4_gemm.argtypes = [P, P, P, I64, I64, I64, P, P, I32, P, P, P, P, I32, I64, P]
     lib.nvfp4_w4a4_linear.restype = I32
     lib.nvfp4_w4a4_linear.argtypes = [P, I32, I64, I64, I64, P, P, I64, P, P, I32, P, P, P, P, I32, I64, P, P, P]
+    lib.nvfp4_requantize_weight.restype = I32
+    lib.nvfp4_requantize_weight.argtypes = [P, P, I64, I64, I32, P, P, P, P, P, P, P]
+    lib.nvfp4_segment_mismatch_factor.restype = I32
+    lib.nvfp4_segment_mismatch_factor.argtypes = [I32, P, ctypes.c_float, P, P]
     return lib
 
 
@@ -176,3 +180,27 @@ def nvfp4_w4a4_linear(x, gscale_in, gscale_out, w_codes, w_scales, seg_end, w_se
                                  N, w_codes.data_ptr(), w_scales.data_ptr(), n_seg, seg, w_seg_gscale.data_ptr(),
                                  ctypes.byref(g) if g is not None else None, y.data_ptr(), _dtype_code(y), ldy,
                                  _ptr(a_codes_out), _ptr(a_scales_out), _stream(stream)))
+
+
+def nvfp4_requantize_weight(codes, scales, seg_end, seg_gscale, gscale_shared, codes_out, scales_out, gscale_out,
+                            stream=None) -> None:
+    """Re-encode a packed weight with per-segment global scales (device seg_gscale)
+    onto one shared scale (device 1-element tensor, or None: the largest segment
+    scale).  codes_out/scales_out may be codes/scales themselves (in place)."""
+    N, half_k = codes.shape
+    seg, n_seg = _seg_array(seg_end)
+    _check(lib.nvfp4_requantize_weight(codes.data_ptr(), scales.data_ptr(), N, 2 * half_k, n_seg, seg,
+                                       seg_gscale.data_ptr(), _ptr(gscale_shared), codes_out.data_ptr(),
+                                       scales_out.data_ptr(), gscale_out.data_ptr(), _stream(stream)))
+
+
+def nvfp4_segment_mismatch_factor(seg_gscale: Sequence[float], g_used: float):
+    """(worst factor, segment index) by which a single-scale fused GEMM using g_used
+    would mis-scale a weight packed with the host segment scales seg_gscale."""
+    n = len(seg_gscale)
+    arr = (ctypes.c_float * n)(*[float(v) for v in seg_gscale])
+    f = ctypes.c_double(0.0)
+    w = ctypes.c_int32(0)
+    _check(lib.nvfp4_segment_mismatch_factor(n, arr, ctypes.c_float(g_used), ctypes.byref(f), ctypes.byref(w)))
+    return f.value, w.value
+

@@ -318,4 +318,57 @@ int32_t nvfp4_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, 
   return hip_status(nvfp4::launch_gemm_tiled(g, s), "nvfp4_w4a4_linear gemm launch");
 }
 
+int32_t nvfp4_requantize_weight(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, int32_t n_seg,
+                                const int64_t* seg_end, const float* seg_gscale, const float* gscale_shared,
+                                uint8_t* codes_out, uint8_t* scales_out, float* gscale_out, void* stream) {
+  if (N <= 0 || K <= 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "N, K must be positive (N=%lld K=%lld)", (long long)N, (long long)K);
+  if (K % 16) return fail(NVFP4_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
+  int32_t st = check_packed(codes, scales, "weight");
+  if (st) return st;
+  st = check_packed(codes_out, scales_out, "output");
+  if (st) return st;
+  if (!seg_gscale) return fail(NVFP4_ERR_INVALID_ARG, "seg_gscale is NULL");
+  if (!gscale_out) return fail(NVFP4_ERR_INVALID_ARG, "gscale_out is NULL");
+  // in place, or no overlap at all (a partial overlap would let one lane read bytes
+  // that another has already rewritten)
+  const uintptr_t cb = (uintptr_t)codes, co = (uintptr_t)codes_out, sb = (uintptr_t)scales, so = (uintptr_t)scales_out;
+  const uintptr_t ncode = (uintptr_t)(N * (K / 2)), nscale = (uintptr_t)(N * (K / 16));
+  if (cb != co && cb < co + ncode && co < cb + ncode)
+    return fail(NVFP4_ERR_INVALID_ARG, "codes_out partially overlaps codes");
+  if (sb != so && sb < so + nscale && so < sb + nscale)
+    return fail(NVFP4_ERR_INVALID_ARG, "scales_out partially overlaps scales");
+  nvfp4::SegTable seg;
+  st = build_seg(n_seg, seg_end, N, nullptr, &seg);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  return hip_status(nvfp4::launch_requantize(codes, scales, N, K, seg, seg_gscale, gscale_shared, codes_out,
+                                             scales_out, gscale_out, static_cast<hipStream_t>(stream)),
+                    "nvfp4_requantize_weight launch");
+}
+
+int32_t nvfp4_segment_mismatch_factor(int32_t n_seg, const float* seg_gscale, float g_used, double* factor_out,
+                                      int32_t* worst_out) {
+  if (n_seg < 1 || n_seg > NVFP4_MAX_SEGMENTS)
+    return fail(NVFP4_ERR_INVALID_ARG, "n_seg=%d outside [1, %d]", n_seg, NVFP4_MAX_SEGMENTS);
+  if (!seg_gscale) return fail(NVFP4_ERR_INVALID_ARG, "seg_gscale is NULL");
+  if (!std::isfinite(g_used) || !(g_used > 0.0f)) return fail(NVFP4_ERR_INVALID_ARG, "g_used must be finite and > 0");
+  double worst = 0.0;
+  int32_t at = 0;
+  for (int32_t i = 0; i < n_seg; ++i) {
+    const float g = seg_gscale[i];
+    if (!std::isfinite(g) || !(g > 0.0f)) return fail(NVFP4_ERR_INVALID_ARG, "segment scale %d must be finite and > 0", i);
+    const double r = (double)g_used / (double)g;
+    const double f = r >= 1.0 ? r : 1.0 / r;
+    if (f > worst) {
+      worst = f;
+      at = i;
+    }
+  }
+  if (factor_out) *factor_out = worst;
+  if (worst_out) *worst_out = at;
+  return ok();
+}
+
 }  // extern "C"

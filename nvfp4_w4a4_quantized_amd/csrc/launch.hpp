@@ -75,4 +75,11 @@ bool gemv_stream_fits(int64_t M, int64_t K, InType t);
 bool linear_skinny_fits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_linear_skinny(const GemvArgs& a, hipStream_t s);
 
+// requant.hip: re-encode a packed weight [N][K] with per-segment global scales
+// (device seg_gscale) onto one shared scale (device gscale_shared, or NULL: the
+// largest segment scale); in place allowed; the shared scale goes to gscale_out.
+hipError_t launch_requantize(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, const SegTable& seg,
+                             const float* seg_gscale, const float* gscale_shared, uint8_t* codes_out,
+                             uint8_t* scales_out, float* gscale_out, hipStream_t s);
+
 }  // namespace nvfp4

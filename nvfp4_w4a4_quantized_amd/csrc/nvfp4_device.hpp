@@ -50,12 +50,10 @@ __device__ __forceinline__ float global_scale_from_amax(float amax) {
   return (float)((double)amax / 2688.0);
 }
 
-// Exact E4M3 block-scale byte for block amax a >= 0 under global scale g >= 0, by
-// float64 division (the reference path).  Inlined on purpose: a call would make the
-// compiler wait for every outstanding memory operation (vmcnt(0)) at the call site.
-__device__ __forceinline__ uint32_t block_scale_byte_exact(float a, float g) {
-  if (!(a > 0.0f) || !(g > 0.0f)) return 0u;
-  const double t = (double)a / (6.0 * (double)g);
+// E4M3 byte of a float64 block-scale quotient t >= 0 (t within 2^-53 relative of
+// the exact quotient, which is never that close to an E4M3 midpoint unless equal
+// to it): round-to-nearest-even, saturated at 448.
+__device__ __forceinline__ uint32_t e4m3_byte_of_quotient(double t) {
   if (t >= 448.0) return 0x7Eu;                    // saturate at the largest finite value
   if (t <= 0x1p-10) return 0u;                      // nearer to 0 than to 2^-9 (tie -> even 0)
   if (t < 0x1p-6) {                                 // subnormal range: multiples of 2^-9
@@ -66,6 +64,14 @@ __device__ __forceinline__ uint32_t block_scale_byte_exact(float a, float g) {
   const int e = (int)((bits >> 52) & 0x7FF) - 1023;          // -6 .. 8
   const uint32_t m3 = (uint32_t)((bits >> 49) & 7ull);
   return ((uint32_t)(e + 7) << 3) | m3;                      // <= 0x7E because t < 448
+}
+
+// Exact E4M3 block-scale byte for block amax a >= 0 under global scale g >= 0, by
+// float64 division (the reference path).  Inlined on purpose: a call would make the
+// compiler wait for every outstanding memory operation (vmcnt(0)) at the call site.
+__device__ __forceinline__ uint32_t block_scale_byte_exact(float a, float g) {
+  if (!(a > 0.0f) || !(g > 0.0f)) return 0u;
+  return e4m3_byte_of_quotient((double)a / (6.0 * (double)g));
 }
 
 // Per-tensor constants of the fast block-scale path.

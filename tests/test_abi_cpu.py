@@ -120,3 +120,40 @@ def test_binding_rejects_wrong_dtype(nv):
     x = torch.zeros((4, 64), dtype=torch.float16)
     with pytest.raises(nv.Nvfp4Error):
         nv.nvfp4_quantize_act(x, None, x, x, x)
+
+
+def test_requantize_weight_validation(nv):
+    def call(N=96, K=64, seg_vals=(48, 96), codes=FAKE, scales=FAKE, sg=FAKE, co=None, so=None, gout=FAKE):
+        seg, n = _segs(list(seg_vals))
+        co = ctypes.c_void_p((1 << 24)) if co is None else co
+        so = ctypes.c_void_p((1 << 25)) if so is None else so
+        return nv.lib.nvfp4_requantize_weight(codes, scales, N, K, n, seg, sg, None, co, so, gout, None)
+    assert call(K=40) == nv.NVFP4_ERR_INVALID_ARG and "multiple of 16" in nv.nvfp4_last_error()
+    assert call(N=0, seg_vals=(1,)) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(seg_vals=(48, 90)) == nv.NVFP4_ERR_INVALID_ARG and "equal N" in nv.nvfp4_last_error()
+    assert call(codes=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(sg=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(gout=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(co=FAKE_ODD) == nv.NVFP4_ERR_UNSUPPORTED
+    # output codes starting 16 bytes into the input codes: a partial overlap
+    assert call(co=ctypes.c_void_p(FAKE.value + 16)) == nv.NVFP4_ERR_INVALID_ARG and "overlap" in nv.nvfp4_last_error()
+    assert call(so=ctypes.c_void_p(FAKE.value + 16)) == nv.NVFP4_ERR_INVALID_ARG and "overlap" in nv.nvfp4_last_error()
+
+
+def test_segment_mismatch_factor_matches_oracle(nv):
+    import numpy as np
+    from oracle import nvfp4 as O
+    rng = np.random.default_rng(3)
+    cases = [([1.5e-5, 6.0e-5], 1.5e-5), ([2.0, 2.0, 2.0], 2.0), ([1.0, 3.0, 0.25], 1.0)]
+    cases += [(list(rng.uniform(1e-6, 1e-3, size=n).astype(np.float32)), float(np.float32(rng.uniform(1e-6, 1e-3))))
+              for n in (1, 4, 64)]
+    for g, used in cases:
+        f, worst = nv.nvfp4_segment_mismatch_factor(g, used)
+        of, ow = O.segment_mismatch_factor(g, used)
+        assert worst == ow and f == of, (g, used, f, of)
+    with pytest.raises(nv.Nvfp4Error):
+        nv.nvfp4_segment_mismatch_factor([1.0, float("inf")], 1.0)
+    with pytest.raises(nv.Nvfp4Error):
+        nv.nvfp4_segment_mismatch_factor([1.0], 0.0)
+    with pytest.raises(nv.Nvfp4Error):
+        nv.nvfp4_segment_mismatch_factor([1.0] * 65, 1.0)
