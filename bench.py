@@ -258,6 +258,57 @@ def time_config(nv, name, steps, warmup):
     return out
 
 
+REQUANT_WORKLOADS = ["gdn_in_proj_8192x16384x5120", "mlp_gate_up_32768x34816x5120"]
+
+
+def time_requantize(nv, name, steps, warmup):
+    """Re-encoding of a fused weight onto one shared global scale
+    (nvfp4_requantize_weight, out of place): back-to-back calls with HIP events
+    around them on the launch stream; GB/s of the algorithmic bytes (packed weight
+    read + written once)."""
+    import torch
+    from synth import workloads as W
+    wl = W.generate(name, M=1)
+    seg_g = None
+    if wl.seg_scale_ratio is not None:
+        _, _, _, wg0 = setup_layer(nv, wl)
+        g0 = float(wg0[0].item())
+        seg_g = [float(np.float32(r) * np.float32(g0)) for r in wl.seg_scale_ratio]
+    _, wc, ws, wg = setup_layer(nv, wl, seg_g)
+    wl.data.clear()
+    N, K = wl.N, wl.K
+    alg = 2 * (N * K // 2 + N * K // 16)
+    # rotated input/output sets: the working set exceeds twice the 256 MB infinity cache
+    n_sets = max(2, -(-600_000_000 // alg))
+    sets = [((wc, ws) if i == 0 else (wc.clone(), ws.clone())) + nv.empty_packed(N, K, "cuda") for i in range(n_sets)]
+    gout = torch.empty(1, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        c, sc, co, so = sets[i % n_sets]
+        nv.nvfp4_requantize_weight(c, sc, wl.seg_end, wg, None, co, so, gout, stream=stream)
+
+    for i in range(warmup):
+        call(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kept = float((sets[0][2] == wc).float().mean().item())
+    gbps = alg / (ms * 1e-3) / 1e9
+    del wc, ws, sets
+    torch.cuda.empty_cache()
+    return dict(workload=f"requantize_weight_{N}x{K}", source=name, segments=wl.seg_end,
+                segment_scales="calibrated, 4x apart" if seg_g else "per-segment amax",
+                us_per_call=round(ms * 1e3, 2), rotated_sets=n_sets, algorithmic_bytes=alg, bound="hbm",
+                gbps=round(gbps, 1),
+                frac_hbm=round(gbps / PEAK_HBM_GBPS, 4), codes_kept_fraction=round(kept, 6))
+
+
 def profile_target(nv, target, launches):
     """Launch one kernel of the path a few times and nothing else, for counter runs
     (rocprofv3 --pmc): first a plain copy of COPY_BYTES (the calibration kernel whose
@@ -266,7 +317,8 @@ def profile_target(nv, target, launches):
       gemm   - nvfp4_w4a4_gemm on the GDN in_proj workload (8192 x 16384 x 5120)
       quant  - nvfp4_quantize_act on the same activations (static scale)
       decode - nvfp4_w4a4_linear, decode GEMV 4 x 16384 x 5120
-      gates  - nvfp4_w4a4_linear, fused GDN gates 32768 x 96 x 5120"""
+      gates  - nvfp4_w4a4_linear, fused GDN gates 32768 x 96 x 5120
+      requant - nvfp4_requantize_weight on the GDN in_proj weight (16384 x 5120)"""
     import torch
     from synth import workloads as W
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
@@ -276,7 +328,8 @@ def profile_target(nv, target, launches):
     torch.cuda.synchronize()
     del src, dst
     name = {"gemm": "gdn_in_proj_8192x16384x5120", "quant": "gdn_in_proj_8192x16384x5120",
-            "decode": "decode_gemv_4x16384x5120", "gates": "gdn_gates_32768x96x5120"}[target]
+            "decode": "decode_gemv_4x16384x5120", "gates": "gdn_gates_32768x96x5120",
+            "requant": "gdn_in_proj_8192x16384x5120"}[target]
     wl = W.generate(name)
     xt, wc, ws, wg = setup_layer(nv, wl)
     M, N, K = wl.M, wl.N, wl.K
@@ -289,8 +342,11 @@ def profile_target(nv, target, launches):
     if wl.gate_heads:
         gate = (torch.from_numpy(wl.data["A_log"]).cuda(), torch.from_numpy(wl.data["dt_bias"]).cuda())
     torch.cuda.synchronize()
+    co, so = nv.empty_packed(N, K, "cuda")
     for _ in range(launches):
-        if target == "gemm":
+        if target == "requant":
+            nv.nvfp4_requantize_weight(wc, ws, wl.seg_end, wg, None, co, so, gout)
+        elif target == "gemm":
             nv.nvfp4_w4a4_gemm(ac, as_, g, wc, ws, wl.seg_end, wg, y)
         elif target == "quant":
             nv.nvfp4_quantize_act(xt, g, ac, as_, gout)
@@ -343,7 +399,7 @@ def main():
     ap.add_argument("--decode-only", action="store_true", help="time only the decode GEMV (no JSON contract line)")
     ap.add_argument("--no-configs", action="store_true", help="skip the GDN-gates and MLP gate/up workloads")
     ap.add_argument("--configs-only", action="store_true", help="time only the GDN-gates and MLP gate/up workloads")
-    ap.add_argument("--profile-target", choices=["gemm", "quant", "decode", "gates"],
+    ap.add_argument("--profile-target", choices=["gemm", "quant", "decode", "gates", "requant"],
                     help="for counter runs: a calibration copy, then a few launches of one kernel (no JSON line)")
     ap.add_argument("--launches", type=int, default=3)
     args = ap.parse_args()
@@ -364,8 +420,9 @@ def main():
         print(json.dumps({"decode": time_decode(nv, args.steps, args.warmup)}), flush=True)
         return
     if args.configs_only:
-        print(json.dumps({"other_workloads": [time_config(nv, n, args.steps, args.warmup) for n in OTHER_WORKLOADS]}),
-              flush=True)
+        ow = [time_config(nv, n, args.steps, args.warmup) for n in OTHER_WORKLOADS]
+        ow += [time_requantize(nv, n, max(args.steps, 20), 5) for n in REQUANT_WORKLOADS]
+        print(json.dumps({"other_workloads": ow}), flush=True)
         return
     log("generating the GDN in_proj workload (8192 x 16384 x 5120)")
     wl = W.generate("gdn_in_proj_8192x16384x5120")
@@ -421,6 +478,10 @@ def main():
         for n in OTHER_WORKLOADS:
             log(f"timing {n}")
             out["other_workloads"].append(time_config(nv, n, args.steps, args.warmup))
+    if not args.no_configs:
+        for n in REQUANT_WORKLOADS:
+            log(f"timing the shared-scale re-encoding of the {n} weight")
+            out["other_workloads"].append(time_requantize(nv, n, max(args.steps, 20), 5))
     if not args.no_cpu:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(wl, np.float32(gstat.item()))

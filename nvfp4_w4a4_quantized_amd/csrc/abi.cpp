@@ -338,6 +338,7 @@ int32_t nvfp4_requantize_weight(const uint8_t* codes, const uint8_t* scales, int
     return fail(NVFP4_ERR_INVALID_ARG, "codes_out partially overlaps codes");
   if (sb != so && sb < so + nscale && so < sb + nscale)
     return fail(NVFP4_ERR_INVALID_ARG, "scales_out partially overlaps scales");
+  if (N * (K / 16) >= (int64_t(1) << 31)) return fail(NVFP4_ERR_UNSUPPORTED, "N * K / 16 must be < 2^31");
   nvfp4::SegTable seg;
   st = build_seg(n_seg, seg_end, N, nullptr, &seg);
   if (st) return st;

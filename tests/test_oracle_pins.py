@@ -488,3 +488,21 @@ def test_segment_mismatch_factor():
     assert O.segment_mismatch_factor(np.full(3, g[0]), g[0]) == (1.0, 0)
     f, worst = O.segment_mismatch_factor(np.array([1.0, 3.0, 0.25], dtype=np.float32), 1.0)
     assert (f, worst) == (4.0, 2)
+
+
+def test_requantize_code_table_identity_range():
+    """The kept-codes range used by the re-encoding kernel: with rho = s g_s /
+    (s' g_shared), every E2M1 magnitude v has RNE(v rho) = v exactly when
+    7/8 <= rho < 7/6 (checked by exact rational rounding at the ends, just outside
+    them and inside)."""
+    mags = [Fraction(E2M1_GOLDEN[c]) for c in range(8)]
+
+    def kept(rho):
+        return all(_nearest_even(_E2M1_MAGS_F, min(v * rho, Fraction(6))) == c for c, v in enumerate(mags))
+
+    eps = Fraction(1, 2 ** 40)
+    assert kept(Fraction(7, 8)) and kept(Fraction(7, 6) - eps) and kept(Fraction(1))
+    assert not kept(Fraction(7, 8) - eps) and not kept(Fraction(7, 6))
+    for k in range(1, 50):
+        rho = Fraction(7, 8) + (Fraction(7, 6) - Fraction(7, 8)) * k / 50
+        assert kept(rho)
