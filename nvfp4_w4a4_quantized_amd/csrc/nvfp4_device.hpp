@@ -186,8 +186,9 @@ __device__ __forceinline__ uint32_t cvt8_fp4(const float* y) {
 // E2M1 midpoint m, between the codes dn and dn + 1: the sign of |x| - m s g, from one
 // fma (m s has <= 7 significant bits, so -(m s) is exact and m s * g + |x| is rounded
 // once and keeps its sign), says on which side q lies; an exact tie goes to the even
-// code.  Such elements are handled per element position with a wave-uniform test, the
-// decision taken branch-free for all lanes.  Blocks whose s g or 1/(s g) is not a
+// code.  The positions holding such an element in any lane of the wave are found as
+// one wave-uniform mask (the OR of the element masks of the lanes that have one);
+// at each flagged position the decision is taken branch-free for all lanes.  Blocks whose s g or 1/(s g) is not a
 // normal fp32 value (extreme scales) are recomputed in float64; the empty asm makes
 // s opaque there, so the compiler cannot hoist the float64 product into the common
 // path.
@@ -215,12 +216,26 @@ __device__ __forceinline__ void quant_block(const float v[NV], const BlockConsts
       const uint32_t c = e2m1_code_exact(v[i], h);
       w[i / 8] = (w[i / 8] & ~(0xFu << (4 * (i % 8)))) | (c << (4 * (i % 8)));
     }
-  } else if (__builtin_amdgcn_ballot_w64(diff != 0u) != 0u) {
+  } else if (uint64_t lanes = __builtin_amdgcn_ballot_w64(diff != 0u)) {
+    // element mask of this lane: bit 4e (word 0) / 4e + 1 (word 1) set where the
+    // bracket codes of element e / 8 + e differ; OR-ed over the few lanes that have
+    // any (one readlane each), so that untaken positions cost only a scalar test
+    uint32_t m = 0;
+#pragma unroll
+    for (int d = 0; d < NV / 8; ++d) {
+      const uint32_t x = w[d] ^ wh[d];
+      m |= ((x | (x >> 1) | (x >> 2) | (x >> 3)) & 0x11111111u) << d;
+    }
+    uint32_t all = 0;
+    while (lanes) {
+      all |= __builtin_amdgcn_readlane(m, __builtin_ctzll(lanes));
+      lanes &= lanes - 1;
+    }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int d = i / 8, sh = 4 * (i % 8);
-      const uint32_t dn = (w[d] >> sh) & 7u, up = (wh[d] >> sh) & 7u;
-      if (__builtin_amdgcn_ballot_w64(dn != up) != 0u) {
+      if (all & (1u << (sh + d))) {                            // wave-uniform
+        const uint32_t dn = (w[d] >> sh) & 7u, up = (wh[d] >> sh) & 7u;
         // midpoint between codes dn and dn + 1, times 4: 1 3 5 7 10 14 20 (dn = 0 .. 6)
         const uint32_t m4 = __builtin_amdgcn_perm(0x00140E0Au, 0x07050301u, dn) & 0xFFu;
         const float r = __builtin_fmaf(-((float)m4 * b.s4), g, __builtin_fabsf(v[i]));
