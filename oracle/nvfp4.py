@@ -436,3 +436,58 @@ def segment_mismatch_factor(g_seg, g_used):
     f = np.maximum(u / g, g / u)
     worst = int(np.argmax(f))
     return float(f[worst]), worst
+
+
+# ----------------------------------------------------------------------------
+# MXFP4: the next format the pages name (E2M1 elements, one power-of-two scale
+# per 32 elements)
+# ----------------------------------------------------------------------------
+#
+# [GDN-4bit review, future work (the paper's section 9 / "range extension"):
+# generalize beyond NVFP4 to FP6 and MXFP.]  The pages name the format only.
+# Readings (the public OCP Microscaling format definition, not the pages):
+# M1  block = 32 consecutive elements of a row; scale = E8M0 byte b (value
+#     2^(b - 127)); elements E2M1 as in R1, packed as in R6.
+# M2  shared exponent = floor(log2(amax_block)) - 2 (2 = exponent of E2M1's
+#     largest value 6 = 1.5 * 2^2), clamped to [-127, 127]; a zero block gets
+#     byte 0 and magnitude codes 0.
+# M3  element code = RNE of x / 2^shared onto the E2M1 magnitudes (ties to even),
+#     saturated at 6 (quotients in [6, 8) occur), sign bit = sign bit of x.
+# M4  no global scale; GEMM Y = deq(A) deq(W)^T in float64, rounded once (R8).
+
+MX_BLOCK = 32
+
+
+def mx_quantize_rows(x64):
+    """MXFP4-quantize the rows of x64 [R, K] (float64 of exact fp32/bf16 inputs,
+    K % 32 == 0).  Returns (codes uint8 [R, K/2], scales uint8 [R, K/32]).
+    Steps: per 32-element block the largest magnitude sets the shared power of
+    two (M2), every element is rounded onto E2M1 under it (M3), then packed (R6)."""
+    x64 = np.asarray(x64, dtype=np.float64)
+    R, K = x64.shape
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    blocks = x64.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(blocks), axis=2)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))        # amax = m 2^e, 0.5 <= m < 1
+    shared = np.clip(e - 1 - 2, -127, 127)                 # floor(log2 amax) - 2
+    shared = np.where(amax > 0, shared, -127)
+    q = np.abs(blocks) / np.ldexp(1.0, shared)[:, :, None]  # exact: division by a power of two
+    mag = e2m1_rne_sat(q)
+    sign = np.signbit(blocks).astype(np.int64)
+    code = ((sign << 3) | mag).reshape(R, K)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (shared + 127).astype(np.uint8)
+
+
+def mx_dequantize_rows(packed, scales):
+    """x_hat = e2m1 * 2^(scale byte - 127), exact in float64."""
+    codes = unpack_codes(packed)
+    R, K = codes.shape
+    s = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127).reshape(R, K // MX_BLOCK, 1)
+    return (e2m1_value(codes).reshape(R, K // MX_BLOCK, MX_BLOCK) * s).reshape(R, K)
+
+
+def mx_gemm_f64(a_codes, a_scales, w_codes, w_scales):
+    """Y64 = deq(A) @ deq(W)^T in float64 (M4)."""
+    return mx_dequantize_rows(a_codes, a_scales) @ mx_dequantize_rows(w_codes, w_scales).T

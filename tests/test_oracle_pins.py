@@ -506,3 +506,80 @@ def test_requantize_code_table_identity_range():
     for k in range(1, 50):
         rho = Fraction(7, 8) + (Fraction(7, 6) - Fraction(7, 8)) * k / 50
         assert kept(rho)
+
+
+# --------------------------------------------------------------------------- MXFP4
+
+def brute_mx_quantize(rows):
+    """Exact rational MXFP4 quantization: the shared exponent from the exact binary
+    exponent of the block maximum, codes by exhaustive nearest-even search."""
+    codes_all, scales_all = [], []
+    for row in rows:
+        codes, scales = [], []
+        for b0 in range(0, len(row), 32):
+            blk = [Fraction(float(v)) for v in row[b0:b0 + 32]]
+            a = max(abs(v) for v in blk)
+            if a == 0:
+                e = -127
+            else:
+                e = 0
+                while Fraction(2) ** (e + 1) <= a:
+                    e += 1
+                while Fraction(2) ** e > a:
+                    e -= 1
+                e = max(-127, min(127, e - 2))
+            scales.append(e + 127)
+            X = Fraction(2) ** e
+            for v, vf in zip(blk, row[b0:b0 + 32]):
+                sign = 8 if math.copysign(1.0, float(vf)) < 0 else 0
+                codes.append(sign | _nearest_even(_E2M1_MAGS_F, min(abs(v) / X, Fraction(6))))
+        codes_all.append([codes[i] | (codes[i + 1] << 4) for i in range(0, len(codes), 2)])
+        scales_all.append(scales)
+    return np.array(codes_all, dtype=np.uint8), np.array(scales_all, dtype=np.uint8)
+
+
+def test_mx_quantize_brute_force():
+    rng = np.random.default_rng(51)
+    x = rng.standard_normal((6, 128)).astype(np.float32) * np.float32(3.0)
+    x[1, :32] *= np.float32(1e-30)                         # tiny block (large negative exponent)
+    x[2, 32:64] = 0.0                                      # zero block
+    x[2, 40] = -0.0
+    x[3, 64:96] = np.float32(6.0) * np.float32(2.0 ** 5)   # block of maxima: quotient exactly 6
+    x[4, 0] = np.float32(7.9)                              # quotient just under 8 saturates to 6
+    x[5, :32] = np.float32(2.0 ** 100)                     # large exponent
+    c, s = O.mx_quantize_rows(x.astype(np.float64))
+    bc, bs = brute_mx_quantize(x)
+    assert np.array_equal(c, bc) and np.array_equal(s, bs)
+
+
+def test_mx_scale_rule_and_round_trip():
+    """amax / 2^shared lies in [4, 8) for every non-zero block; values on the grid
+    (e2m1 * 2^e with a block maximum of 4 or 6) re-quantize to the same bytes."""
+    rng = np.random.default_rng(52)
+    x = (rng.standard_normal((16, 256)) * np.exp(rng.uniform(-20, 20, size=(16, 1)))).astype(np.float32)
+    c, s = O.mx_quantize_rows(x.astype(np.float64))
+    amax = np.abs(x.astype(np.float64)).reshape(16, 8, 32).max(axis=2)
+    ratio = amax / np.ldexp(1.0, s.astype(np.int64) - 127)
+    assert np.all((ratio >= 4) & (ratio < 8))
+    xh = O.mx_dequantize_rows(c, s)
+    c2, s2 = O.mx_quantize_rows(xh)
+    top = np.abs(xh).reshape(16, 8, 32).max(axis=2) / np.ldexp(1.0, s.astype(np.int64) - 127)
+    ok = np.isin(top, [4.0, 6.0])                          # blocks whose maximum kept exponent e+2
+    assert ok.mean() > 0.9
+    assert np.array_equal(s2[ok], s[ok])
+    rows_ok = ok.all(axis=1)
+    assert np.array_equal(c2[rows_ok], c[rows_ok])
+
+
+def test_mx_gemm_integer_matmul_at_unit_scale():
+    rng = np.random.default_rng(53)
+    A = rng.choice(np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -.5, -1, -1.5, -2, -3, -4, -6]), size=(5, 64))
+    Wt = rng.choice(np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -6, -4]), size=(7, 64))
+    A[:, ::32] = 6.0                                       # every block max = 6: shared exponent 0
+    Wt[:, ::32] = -6.0
+    ac, as_ = O.mx_quantize_rows(A)
+    wc, ws = O.mx_quantize_rows(Wt)
+    assert np.all(as_ == 127) and np.all(ws == 127)
+    y = O.mx_gemm_f64(ac, as_, wc, ws)
+    Ai, Wi = (A * 2).astype(np.int64), (Wt * 2).astype(np.int64)
+    assert np.array_equal(y * 4, (Ai @ Wi.T).astype(np.float64))
