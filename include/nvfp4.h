@@ -204,6 +204,32 @@ NVFP4_API int32_t nvfp4_requantize_weight(const uint8_t* codes, const uint8_t* s
 NVFP4_API int32_t nvfp4_segment_mismatch_factor(int32_t n_seg, const float* seg_gscale, float g_used,
                                       double* factor_out, int32_t* worst_out);
 
+/*
+ * MXFP4 variant (the format the review page names as the next generalization,
+ * future work / the paper's section 9): E2M1 codes packed as above, one E8M0 scale
+ * byte b (value 2^(b-127)) per 32 elements, no global scale.  The format follows the
+ * public OCP Microscaling definition: b = 127 + clamp(floor(log2 amax_block) - 2,
+ * -127, 127) (byte 0 for a zero block), codes = RNE of x / 2^(b-127) onto the E2M1
+ * magnitudes with ties to even, saturated at 6, sign bit of x.
+ *
+ * Quantization of rows of x (device, [M][ldx], F32 or BF16, K % 32 == 0):
+ *   codes  device [M][K/2], scales device [M][K/32] (outputs)
+ */
+NVFP4_API int32_t nvfp4_mxfp4_quantize(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * MXFP4 GEMM on the native block-scaled FP4 matrix instructions:
+ * y[m,n] = sum_k e2m1 * 2^(sa-127) * e2m1 * 2^(sw-127), fp32 accumulation, rounded
+ * once to y_dtype.
+ *   a_codes, a_scales device [M][K/2], [M][K/32]; w_codes, w_scales device [N][K/2], [N][K/32]
+ *   y device [M][ldy] of y_dtype (F32 or BF16), output
+ *   K % 128 == 0 (NVFP4_ERR_UNSUPPORTED otherwise); each packed operand < 2^31 bytes.
+ */
+NVFP4_API int32_t nvfp4_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M, int64_t N, int64_t K,
+                         const uint8_t* w_codes, const uint8_t* w_scales, void* y, int32_t y_dtype, int64_t ldy,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

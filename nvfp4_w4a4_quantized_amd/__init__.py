@@ -28,7 +28,8 @@ NVFP4_DTYPE_BF16 = 1
 NVFP4_MAX_SEGMENTS = 64
 
 EXPORTED = ["nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize_act", "nvfp4_pack_weight",
-            "nvfp4_w4a4_gemm", "nvfp4_w4a4_linear", "nvfp4_requantize_weight", "nvfp4_segment_mismatch_factor"]
+            "nvfp4_w4a4_gemm", "nvfp4_w4a4_linear", "nvfp4_requantize_weight", "nvfp4_segment_mismatch_factor",
+            "nvfp4_mxfp4_quantize", "nvfp4_mxfp4_gemm"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -63,6 +64,10 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_requantize_weight.argtypes = [P, P, I64, I64, I32, P, P, P, P, P, P, P]
     lib.nvfp4_segment_mismatch_factor.restype = I32
     lib.nvfp4_segment_mismatch_factor.argtypes = [I32, P, ctypes.c_float, P, P]
+    lib.nvfp4_mxfp4_quantize.restype = I32
+    lib.nvfp4_mxfp4_quantize.argtypes = [P, I32, I64, I64, I64, P, P, P]
+    lib.nvfp4_mxfp4_gemm.restype = I32
+    lib.nvfp4_mxfp4_gemm.argtypes = [P, P, I64, I64, I64, P, P, P, I32, I64, P]
     return lib
 
 
@@ -203,4 +208,27 @@ def nvfp4_segment_mismatch_factor(seg_gscale: Sequence[float], g_used: float):
     w = ctypes.c_int32(0)
     _check(lib.nvfp4_segment_mismatch_factor(n, arr, ctypes.c_float(g_used), ctypes.byref(f), ctypes.byref(w)))
     return f.value, w.value
+
+
+def empty_mx_packed(rows: int, K: int, device="cuda"):
+    """Device buffers (codes [rows, K/2], scales [rows, K/32]) for an MXFP4 operand."""
+    torch = _torch()
+    return (torch.empty((rows, K // 2), dtype=torch.uint8, device=device),
+            torch.empty((rows, K // 32), dtype=torch.uint8, device=device))
+
+
+def nvfp4_mxfp4_quantize(x, codes, scales, stream=None) -> None:
+    """MXFP4-quantize x [M, K] (bf16/fp32, K % 32 == 0)."""
+    M, K, ldx = _rows(x, "x")
+    _check(lib.nvfp4_mxfp4_quantize(x.data_ptr(), _dtype_code(x), M, K, ldx, codes.data_ptr(), scales.data_ptr(),
+                                    _stream(stream)))
+
+
+def nvfp4_mxfp4_gemm(a_codes, a_scales, w_codes, w_scales, y, stream=None) -> None:
+    """y = MXFP4 GEMM of packed operands (K % 128 == 0)."""
+    M, half_k = a_codes.shape
+    N = w_codes.shape[0]
+    _, _, ldy = _rows(y, "y")
+    _check(lib.nvfp4_mxfp4_gemm(a_codes.data_ptr(), a_scales.data_ptr(), M, N, 2 * half_k, w_codes.data_ptr(),
+                                w_scales.data_ptr(), y.data_ptr(), _dtype_code(y), ldy, _stream(stream)))
 

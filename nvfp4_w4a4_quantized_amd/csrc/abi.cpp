@@ -372,4 +372,44 @@ int32_t nvfp4_segment_mismatch_factor(int32_t n_seg, const float* seg_gscale, fl
   return ok();
 }
 
+int32_t nvfp4_mxfp4_quantize(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
+                             uint8_t* scales, void* stream) {
+  int32_t st = check_x(x, x_dtype, M, K, ldx, "x");
+  if (st) return st;
+  if (K % 32) return fail(NVFP4_ERR_INVALID_ARG, "K=%lld is not a multiple of 32 (MXFP4 block)", (long long)K);
+  st = check_packed(codes, scales, "mxfp4");
+  if (st) return st;
+  if (M * (K / 32) >= (int64_t(1) << 32)) return fail(NVFP4_ERR_UNSUPPORTED, "M * K / 32 must be < 2^32");
+  st = check_device();
+  if (st) return st;
+  return hip_status(nvfp4::launch_mx_quant(x, in_type(x_dtype), M, K, ldx, codes, scales,
+                                           static_cast<hipStream_t>(stream)),
+                    "nvfp4_mxfp4_quantize launch");
+}
+
+int32_t nvfp4_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M, int64_t N, int64_t K,
+                         const uint8_t* w_codes, const uint8_t* w_scales, void* y, int32_t y_dtype, int64_t ldy,
+                         void* stream) {
+  if (M <= 0 || N <= 0 || K <= 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "M, N, K must be positive (M=%lld N=%lld K=%lld)", (long long)M,
+                (long long)N, (long long)K);
+  if (K % 32) return fail(NVFP4_ERR_INVALID_ARG, "K=%lld is not a multiple of 32 (MXFP4 block)", (long long)K);
+  if (K % 128) return fail(NVFP4_ERR_UNSUPPORTED, "the MXFP4 GEMM needs K %% 128 == 0 (K=%lld)", (long long)K);
+  int32_t st = check_packed(a_codes, a_scales, "a");
+  if (st) return st;
+  st = check_packed(w_codes, w_scales, "w");
+  if (st) return st;
+  if (!y) return fail(NVFP4_ERR_INVALID_ARG, "y is NULL");
+  if (!valid_dtype(y_dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "y dtype %d is not F32 or BF16", y_dtype);
+  if (ldy < N) return fail(NVFP4_ERR_INVALID_ARG, "ldy=%lld < N=%lld", (long long)ldy, (long long)N);
+  if (!aligned16(y)) return fail(NVFP4_ERR_UNSUPPORTED, "y must be 16-byte aligned");
+  if (M * (K / 2) >= (int64_t(1) << 31) || N * (K / 2) >= (int64_t(1) << 31))
+    return fail(NVFP4_ERR_UNSUPPORTED, "each packed operand must be < 2^31 bytes");
+  st = check_device();
+  if (st) return st;
+  return hip_status(nvfp4::launch_mx_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, y,
+                                          y_dtype == NVFP4_DTYPE_BF16, ldy, static_cast<hipStream_t>(stream)),
+                    "nvfp4_mxfp4_gemm launch");
+}
+
 }  // extern "C"

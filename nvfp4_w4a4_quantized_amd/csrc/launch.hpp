@@ -82,4 +82,11 @@ hipError_t launch_requantize(const uint8_t* codes, const uint8_t* scales, int64_
                              const float* seg_gscale, const float* gscale_shared, uint8_t* codes_out,
                              uint8_t* scales_out, float* gscale_out, hipStream_t s);
 
+// mx.hip: MXFP4 quantizer (K % 32 == 0) and GEMM on the scaled FP4 MFMA (K % 128 == 0)
+hipError_t launch_mx_quant(const void* x, InType t, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
+                           uint8_t* scales, hipStream_t s);
+hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
+                          const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y, bool bf16_out,
+                          int64_t ldy, hipStream_t s);
+
 }  // namespace nvfp4

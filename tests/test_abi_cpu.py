@@ -157,3 +157,17 @@ def test_segment_mismatch_factor_matches_oracle(nv):
         nv.nvfp4_segment_mismatch_factor([1.0], 0.0)
     with pytest.raises(nv.Nvfp4Error):
         nv.nvfp4_segment_mismatch_factor([1.0] * 65, 1.0)
+
+
+def test_mxfp4_validation(nv):
+    q = lambda K=64, ld=64, codes=FAKE: nv.lib.nvfp4_mxfp4_quantize(FAKE, 1, 4, K, ld, codes, FAKE, None)
+    assert q(K=48, ld=48) == nv.NVFP4_ERR_INVALID_ARG and "multiple of 32" in nv.nvfp4_last_error()
+    assert q(codes=None) == nv.NVFP4_ERR_INVALID_ARG
+    g = lambda M=4, N=64, K=256, y=FAKE, ldy=64, dt=1: nv.lib.nvfp4_mxfp4_gemm(FAKE, FAKE, M, N, K, FAKE, FAKE, y, dt,
+                                                                                 ldy, None)
+    assert g(K=96) == nv.NVFP4_ERR_UNSUPPORTED and "128" in nv.nvfp4_last_error()
+    assert g(K=80) == nv.NVFP4_ERR_INVALID_ARG
+    assert g(M=0) == nv.NVFP4_ERR_INVALID_ARG
+    assert g(y=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert g(ldy=32) == nv.NVFP4_ERR_INVALID_ARG
+    assert g(dt=9) == nv.NVFP4_ERR_UNSUPPORTED
