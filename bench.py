@@ -309,6 +309,53 @@ def time_requantize(nv, name, steps, warmup):
                 frac_hbm=round(gbps / PEAK_HBM_GBPS, 4), codes_kept_fraction=round(kept, 6))
 
 
+PEAK_MFMA_FP4_TFLOPS = 10100.0         # MI355X dense FP4 MFMA
+
+
+def time_mxfp4(nv, steps, warmup):
+    """MXFP4 variant on the GDN in_proj shape (8192 x 16384 x 5120, bf16 in/out): one
+    step = nvfp4_mxfp4_quantize(x) + nvfp4_mxfp4_gemm, the weight quantized once
+    beforehand; HIP events around each launch on the launch stream."""
+    import torch
+    from synth import workloads as W
+    wl = W.generate("gdn_in_proj_8192x16384x5120")
+    M, N, K = wl.M, wl.N, wl.K
+    xt = dev_bf16(wl.data["x_bf16"])
+    wt = torch.from_numpy(wl.data["w32"]).cuda()
+    wl.data.clear()
+    wc, ws = nv.empty_mx_packed(N, K, "cuda")
+    nv.nvfp4_mxfp4_quantize(wt, wc, ws)
+    del wt
+    ac, as_ = nv.empty_mx_packed(M, K, "cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        nv.nvfp4_mxfp4_quantize(xt, ac, as_, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        nv.nvfp4_mxfp4_gemm(ac, as_, wc, ws, y, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    wall = timed_steps(step, steps)
+    q_ms, g_ms = event_breakdown(step, steps)
+    flops = 2.0 * M * N * K
+    gt = flops / (g_ms * 1e-3) / 1e12
+    del xt, wc, ws, ac, as_, y
+    torch.cuda.empty_cache()
+    return dict(workload="mxfp4_gdn_in_proj_8192x16384x5120", M=M, N=N, K=K,
+                mode="MXFP4 quantize (activation) + GEMM on the block-scaled FP4 MFMA, bf16 out",
+                ms_per_step=round(wall, 4), tflops=round(flops / (wall * 1e-3) / 1e12, 2),
+                breakdown_ms={"mx_quantize": round(q_ms, 4), "mx_gemm": round(g_ms, 4)}, bound="mfma",
+                gemm_tflops=round(gt, 2), peak_fp4_tflops=PEAK_MFMA_FP4_TFLOPS,
+                frac_fp4_peak=round(gt / PEAK_MFMA_FP4_TFLOPS, 4))
+
+
 def profile_target(nv, target, launches):
     """Launch one kernel of the path a few times and nothing else, for counter runs
     (rocprofv3 --pmc): first a plain copy of COPY_BYTES (the calibration kernel whose
@@ -422,6 +469,7 @@ def main():
     if args.configs_only:
         ow = [time_config(nv, n, args.steps, args.warmup) for n in OTHER_WORKLOADS]
         ow += [time_requantize(nv, n, max(args.steps, 20), 5) for n in REQUANT_WORKLOADS]
+        ow.append(time_mxfp4(nv, args.steps, args.warmup))
         print(json.dumps({"other_workloads": ow}), flush=True)
         return
     log("generating the GDN in_proj workload (8192 x 16384 x 5120)")
@@ -479,6 +527,8 @@ def main():
             log(f"timing {n}")
             out["other_workloads"].append(time_config(nv, n, args.steps, args.warmup))
     if not args.no_configs:
+        log("timing the MXFP4 variant on the GDN in_proj shape")
+        out["other_workloads"].append(time_mxfp4(nv, args.steps, args.warmup))
         for n in REQUANT_WORKLOADS:
             log(f"timing the shared-scale re-encoding of the {n} weight")
             out["other_workloads"].append(time_requantize(nv, n, max(args.steps, 20), 5))
