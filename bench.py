@@ -6,8 +6,10 @@ the activation quantization (calibrated activation global scale).  One step =
 nvfp4_quantize_act + nvfp4_w4a4_gemm (quantize, block-scaled GEMM, per-segment
 epilogue).  Also reported: the same with dynamic activation scaling (amax pass
 included), the decode GEMV (M=4, N=16384, K=5120) in GB/s of packed weight
-traffic with weight copies rotated past the 256 MB infinity cache, and the CPU
-oracle's throughput on a bounded row sample of the headline workload.
+traffic with weight copies rotated past the 256 MB infinity cache, the GDN gates
+and MLP gate/up workloads, the shared-scale re-encoding of fused weights, the
+MXFP4 variant on the in_proj shape, and the CPU oracle's throughput on a bounded
+row sample of the headline workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--all]
 """
@@ -365,7 +367,8 @@ def profile_target(nv, target, launches):
       quant  - nvfp4_quantize_act on the same activations (static scale)
       decode - nvfp4_w4a4_linear, decode GEMV 4 x 16384 x 5120
       gates  - nvfp4_w4a4_linear, fused GDN gates 32768 x 96 x 5120
-      requant - nvfp4_requantize_weight on the GDN in_proj weight (16384 x 5120)"""
+      requant - nvfp4_requantize_weight on the GDN in_proj weight (16384 x 5120)
+      mxgemm - nvfp4_mxfp4_gemm on the GDN in_proj shape (MXFP4 operands)"""
     import torch
     from synth import workloads as W
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
@@ -376,7 +379,7 @@ def profile_target(nv, target, launches):
     del src, dst
     name = {"gemm": "gdn_in_proj_8192x16384x5120", "quant": "gdn_in_proj_8192x16384x5120",
             "decode": "decode_gemv_4x16384x5120", "gates": "gdn_gates_32768x96x5120",
-            "requant": "gdn_in_proj_8192x16384x5120"}[target]
+            "requant": "gdn_in_proj_8192x16384x5120", "mxgemm": "gdn_in_proj_8192x16384x5120"}[target]
     wl = W.generate(name)
     xt, wc, ws, wg = setup_layer(nv, wl)
     M, N, K = wl.M, wl.N, wl.K
@@ -390,8 +393,16 @@ def profile_target(nv, target, launches):
         gate = (torch.from_numpy(wl.data["A_log"]).cuda(), torch.from_numpy(wl.data["dt_bias"]).cuda())
     torch.cuda.synchronize()
     co, so = nv.empty_packed(N, K, "cuda")
+    if target == "mxgemm":
+        xc, xs = nv.empty_mx_packed(M, K, "cuda")
+        mwc, mws = nv.empty_mx_packed(N, K, "cuda")
+        nv.nvfp4_mxfp4_quantize(xt, xc, xs)
+        nv.nvfp4_mxfp4_quantize(torch.from_numpy(wl.data["w32"]).cuda(), mwc, mws)
+        torch.cuda.synchronize()
     for _ in range(launches):
-        if target == "requant":
+        if target == "mxgemm":
+            nv.nvfp4_mxfp4_gemm(xc, xs, mwc, mws, y)
+        elif target == "requant":
             nv.nvfp4_requantize_weight(wc, ws, wl.seg_end, wg, None, co, so, gout)
         elif target == "gemm":
             nv.nvfp4_w4a4_gemm(ac, as_, g, wc, ws, wl.seg_end, wg, y)
@@ -446,7 +457,7 @@ def main():
     ap.add_argument("--decode-only", action="store_true", help="time only the decode GEMV (no JSON contract line)")
     ap.add_argument("--no-configs", action="store_true", help="skip the GDN-gates and MLP gate/up workloads")
     ap.add_argument("--configs-only", action="store_true", help="time only the GDN-gates and MLP gate/up workloads")
-    ap.add_argument("--profile-target", choices=["gemm", "quant", "decode", "gates", "requant"],
+    ap.add_argument("--profile-target", choices=["gemm", "quant", "decode", "gates", "requant", "mxgemm"],
                     help="for counter runs: a calibration copy, then a few launches of one kernel (no JSON line)")
     ap.add_argument("--launches", type=int, default=3)
     args = ap.parse_args()
