@@ -224,7 +224,8 @@ NVFP4_API int32_t nvfp4_mxfp4_quantize(const void* x, int32_t x_dtype, int64_t M
  * once to y_dtype.
  *   a_codes, a_scales device [M][K/2], [M][K/32]; w_codes, w_scales device [N][K/2], [N][K/32]
  *   y device [M][ldy] of y_dtype (F32 or BF16), output
- *   K % 128 == 0 (NVFP4_ERR_UNSUPPORTED otherwise); each packed operand < 2^31 bytes.
+ *   K % 128 == 0, even ldy, even N for BF16 output, (M + 264) * ldy * sizeof(y) < 2^32,
+ *   each packed operand < 2^31 bytes (NVFP4_ERR_UNSUPPORTED otherwise).
  */
 NVFP4_API int32_t nvfp4_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M, int64_t N, int64_t K,
                          const uint8_t* w_codes, const uint8_t* w_scales, void* y, int32_t y_dtype, int64_t ldy,

@@ -405,6 +405,11 @@ int32_t nvfp4_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_
   if (!aligned16(y)) return fail(NVFP4_ERR_UNSUPPORTED, "y must be 16-byte aligned");
   if (M * (K / 2) >= (int64_t(1) << 31) || N * (K / 2) >= (int64_t(1) << 31))
     return fail(NVFP4_ERR_UNSUPPORTED, "each packed operand must be < 2^31 bytes");
+  const int64_t esz = y_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+  if (ldy % 2 || (y_dtype == NVFP4_DTYPE_BF16 && N % 2))
+    return fail(NVFP4_ERR_UNSUPPORTED, "the MXFP4 GEMM needs an even ldy (and an even N for bf16 output)");
+  if ((M + 264) * ldy * esz >= (int64_t(1) << 32))
+    return fail(NVFP4_ERR_UNSUPPORTED, "the MXFP4 GEMM output must span < 4 GiB ((M + 264) * ldy * size)");
   st = check_device();
   if (st) return st;
   return hip_status(nvfp4::launch_mx_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, y,

@@ -127,30 +127,6 @@ __device__ __forceinline__ i32x8 fp4_operand(u32x4 c) {
   return i32x8{(int)c[0], (int)c[1], (int)c[2], (int)c[3], 0, 0, 0, 0};
 }
 
-// Edge tiles (rows past M or columns past N): element stores with bounds checks.  Kept
-// out of line so that the interior tiles' epilogue can store straight from the
-// accumulator registers without first copying all of them out.
-template <bool BF16OUT>
-__device__ __attribute__((noinline)) void mx_store_boundary(void* y, int64_t ldy, int64_t M, int64_t N,
-                                                            const f32x16 (&acc)[4][4], int64_t mb, int64_t nb) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = nb + j * 32;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = mb + i * 32 + 8 * (r >> 2) + (r & 3);
-        if (m < M && n < N) {
-          if constexpr (BF16OUT)
-            reinterpret_cast<uint16_t*>(y)[m * ldy + n] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
-          else
-            reinterpret_cast<float*>(y)[m * ldy + n] = acc[i][j][r];
-        }
-      }
-  }
-}
-
 template <bool BF16OUT>
 __global__ __launch_bounds__(256, 1) void k_mx_gemm(MxArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[XST * XS_BYTES];
@@ -263,54 +239,55 @@ __global__ __launch_bounds__(256, 1) void k_mx_gemm(MxArgs a) {
   }
   wait_vmcnt<0>();                      // no direct-to-LDS write may outlive the workgroup
 
-  // Epilogue.  D of block (i, j): lane (h, li) holds column li, rows 8 (r >> 2) + 4 h + (r & 3).
-  // Interior tiles store through a buffer descriptor of y: a per-lane VGPR offset fixed
-  // for the whole epilogue plus a wave-uniform SGPR offset (byte extent < 2^32, checked
-  // here); bf16 pairs of adjacent columns are assembled across neighbouring lanes (DPP)
-  // into 32-bit stores, as in the NVFP4 prefill kernel.
+  // Epilogue, one path for every tile.  D of block (i, j): lane (h, li) holds column li,
+  // rows 8 (r >> 2) + 4 h + (r & 3).  Stores go through a buffer descriptor of y whose
+  // size is y's byte extent: a per-lane VGPR offset fixed for the whole epilogue plus a
+  // wave-uniform SGPR offset.  Rows past M lie at or beyond the extent, so the hardware
+  // drops their stores; columns past N are masked per lane.  The host guarantees that
+  // no offset wraps 32 bits ((M + 264) * ldy * size < 2^32), an even ldy, and for bf16
+  // output an even N (pairs of adjacent columns are stored as one 32-bit word, built
+  // across neighbouring lanes with DPP, as in the NVFP4 prefill kernel).
   constexpr int ESZ = BF16OUT ? 2 : 4;
   const int64_t extent = ((a.M - 1) * a.ldy + a.N) * ESZ;
-  if (m0 + XBM <= a.M && n0 + XBN <= a.N && extent < (int64_t(1) << 32) && (a.ldy % 2) == 0) {
-    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, (int)(uint32_t)extent, 0x00020000);
-    const uint32_t ldyb = (uint32_t)a.ldy * ESZ;
-    const uint32_t tile_off = __builtin_amdgcn_readfirstlane((uint32_t)(m0 + wm * 128) * ldyb + (uint32_t)(n0 + wn * 128) * ESZ);
-    if constexpr (BF16OUT) {
-      const bool odd = (li & 1) != 0;
-      const uint32_t voff = (uint32_t)(4 * h) * ldyb + (uint32_t)li * 2 + (odd ? ldyb - 2 : 0u);
-      const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+  const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, (int)(uint32_t)extent, 0x00020000);
+  const uint32_t ldyb = (uint32_t)a.ldy * ESZ;
+  const uint32_t tile_off = __builtin_amdgcn_readfirstlane((uint32_t)(m0 + wm * 128) * ldyb + (uint32_t)(n0 + wn * 128) * ESZ);
+  const int64_t ncol = n0 + wn * 128 + (BF16OUT ? (li | 1) : li);   // last column this lane writes, block j = 0
+  if constexpr (BF16OUT) {
+    const bool odd = (li & 1) != 0;
+    const uint32_t voff = (uint32_t)(4 * h) * ldyb + (uint32_t)li * 2 + (odd ? ldyb - 2 : 0u);
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      const bool col_ok = ncol + 32 * j < a.N;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int p = 0; p < 8; ++p) {
-            typedef float f32x2 __attribute__((ext_vector_type(2)));
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            const f32x2 v = {acc[i][j][2 * p], acc[i][j][2 * p + 1]};
-            const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-            const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp((int)pk, (int)pk, 0xB1, 0xF, 0xF, false);
-            const uint32_t word = __builtin_amdgcn_perm(nb, pk, sel);
-            const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (p >> 1) + 2 * (p & 1)) * ldyb + (uint32_t)(j * 64);
-            __builtin_amdgcn_raw_buffer_store_b32(word, yr, voff, soff, 0);
-            // one column block at a time: keeps the accumulator copies of the
-            // conversion to 16 per lane instead of all 256 at once
-            if (p == 7) __builtin_amdgcn_sched_barrier(0);
-          }
-    } else {
-      const uint32_t voff = (uint32_t)(4 * h) * ldyb + (uint32_t)li * 4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldyb + (uint32_t)(j * 128);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), yr, voff, soff, 0);
-          }
+        for (int p = 0; p < 8; ++p) {
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          const f32x2 v = {acc[i][j][2 * p], acc[i][j][2 * p + 1]};
+          const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+          const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp((int)pk, (int)pk, 0xB1, 0xF, 0xF, false);
+          const uint32_t word = __builtin_amdgcn_perm(nb, pk, sel);
+          const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (p >> 1) + 2 * (p & 1)) * ldyb + (uint32_t)(j * 64);
+          if (col_ok) __builtin_amdgcn_raw_buffer_store_b32(word, yr, voff, soff, 0);
+        }
     }
-    return;
+  } else {
+    const uint32_t voff = (uint32_t)(4 * h) * ldyb + (uint32_t)li * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool col_ok = ncol + 32 * j < a.N;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldyb + (uint32_t)(j * 128);
+          if (col_ok) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), yr, voff, soff, 0);
+        }
+    }
   }
-  mx_store_boundary<BF16OUT>(a.y, a.ldy, a.M, a.N, acc, m0 + wm * 128 + 4 * h, n0 + wn * 128 + li);
 }
 
 }  // namespace

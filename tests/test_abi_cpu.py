@@ -171,3 +171,6 @@ def test_mxfp4_validation(nv):
     assert g(y=None) == nv.NVFP4_ERR_INVALID_ARG
     assert g(ldy=32) == nv.NVFP4_ERR_INVALID_ARG
     assert g(dt=9) == nv.NVFP4_ERR_UNSUPPORTED
+    assert g(N=63, ldy=64) == nv.NVFP4_ERR_UNSUPPORTED and "even" in nv.nvfp4_last_error()   # bf16 pairs
+    assert g(N=63, ldy=63, dt=0) == nv.NVFP4_ERR_UNSUPPORTED                                   # odd ldy
+    assert g(M=1 << 20, N=4096, ldy=4096, K=128) == nv.NVFP4_ERR_UNSUPPORTED                  # > 4 GiB output
