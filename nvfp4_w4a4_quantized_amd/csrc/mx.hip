@@ -74,17 +74,22 @@ __global__ __launch_bounds__(256) void k_mx_quant(const void* x, int64_t ldx, in
 // 128 x 128 (4 x 4 MFMA 32x32x64 with FP4 operands, fp32 accumulators in AGPRs).
 // A lane (h, li) feeds row li of a 32-row block with its 16 bytes of codes for
 // elements 32 h .. 32 h + 31 of the K step (= MX block h) and that block's E8M0
-// scale.  Packed tiles (codes 16 KiB + scales 2 KiB per K step) go HBM -> a 4-stage
-// LDS ring by direct-to-LDS loads issued three K steps ahead; operand registers are
-// double-buffered and the barrier sits between the two halves of a K step's MFMAs,
-// so the LDS reads of the next step run under the second half.  Rows past M or N are
+// scale.  Packed tiles go HBM -> LDS by direct-to-LDS loads in slots of four K steps
+// (a row's 128 bytes of codes = one cache line per load, which is what bounds the
+// feed: loads of 32 bytes per row per K step reached only ~4 TB/s of L2->LDS traffic),
+// two slots, the next slot loaded while the current one is consumed; operand registers
+// are double-buffered and the LDS reads of the next step run under the second half of
+// a K step's MFMAs.  Rows past M or N are
 // clamped (never stored).  Requires K % 128 == 0 (an even number of K steps).
 // ---------------------------------------------------------------------------------
 constexpr int XBM = 256, XBN = 256, XBK = 64;
-constexpr int XST = 4;
-// scales: [row][4 B] per stage, the aligned dword of the row's scale bytes that holds
-// the step's two (direct-to-LDS loads give every lane a 4-byte slot)
-constexpr int XS_A = 0, XS_W = 8192, XS_SA = 16384, XS_SW = 17408, XS_BYTES = 18432;
+// LDS ring: 2 slots of 4 K steps (256 elements) each.  Slot layout: codes [row][128 B]
+// (one whole cache line of the row, 16-byte chunk c stored at chunk c ^ (row & 7), so
+// that the per-lane 16-byte reads of 8 consecutive rows hit distinct banks), then the
+// row's 8 scale bytes as two dword planes [dword][row][4 B] (direct-to-LDS loads give
+// every lane a 4-byte slot).
+constexpr int XSS = 4;                                  // K steps per slot
+constexpr int XS_A = 0, XS_W = 32768, XS_SA = 65536, XS_SW = 67584, XS_BYTES = 69632;
 
 struct MxArgs {
   const uint8_t* a_codes;
@@ -129,7 +134,7 @@ __device__ __forceinline__ i32x8 fp4_operand(u32x4 c) {
 
 template <bool BF16OUT>
 __global__ __launch_bounds__(256, 1) void k_mx_gemm(MxArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[XST * XS_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * XS_BYTES];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -140,20 +145,22 @@ __global__ __launch_bounds__(256, 1) void k_mx_gemm(MxArgs a) {
   const int64_t m0 = bm * XBM, n0 = bn * XBN;
   const int64_t K = a.K, kh = K >> 1, kbs = K >> 5;
 
-  // load roles: 2 x 32 rows of A and of W codes per wave (lanes 2j, 2j+1: the two
-  // 16-byte halves of one row, stored swapped when bit 2 xor bit 3 of the row is set),
-  // 64 rows of A and of W scales (the aligned dword holding the step's 2 bytes; rows
-  // hold K/32 scale bytes, a multiple of 4 since K % 128 == 0)
-  uint32_t oa_c[2], ow_c[2], lo_c[2];
+  // load roles per slot: 64 rows of A and of W codes per wave, 8 rows per instruction
+  // (lane l: row 8 q + l / 8 of the wave's 64, physical chunk l % 8 = logical chunk
+  // (l % 8) ^ (row & 7): each row's 128 bytes come from one cache line), and the
+  // wave's 64 rows of A and of W scales (two dwords per row).  Rows past M or N are
+  // clamped (in bounds; never stored); bytes past a row's end (last, partial slot)
+  // are never read by the MFMAs, and past the buffer the descriptor returns zero.
+  const int lrow = lane >> 3, lchunk = lane & 7;
+  uint32_t oa_c[8], ow_c[8];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r0 = 32 * (2 * wave + q);
-    const int row = r0 + (lane >> 1);
-    const int hl = (lane & 1) ^ (((row >> 2) ^ (row >> 3)) & 1);
-    oa_c[q] = (uint32_t)(min<int64_t>(m0 + row, a.M - 1) * kh + 16 * hl);
-    ow_c[q] = (uint32_t)(min<int64_t>(n0 + row, a.N - 1) * kh + 16 * hl);
-    lo_c[q] = (uint32_t)(r0 * 32);
+  for (int q = 0; q < 8; ++q) {
+    const int row = 64 * wave + 8 * q + lrow;
+    const int c = lchunk ^ (row & 7);
+    oa_c[q] = (uint32_t)(min<int64_t>(m0 + row, a.M - 1) * kh + 16 * c);
+    ow_c[q] = (uint32_t)(min<int64_t>(n0 + row, a.N - 1) * kh + 16 * c);
   }
+  const uint32_t lo_c = (uint32_t)(64 * wave * 128);
   const uint32_t oa_s = (uint32_t)(min<int64_t>(m0 + 64 * wave + lane, a.M - 1) * kbs);
   const uint32_t ow_s = (uint32_t)(min<int64_t>(n0 + 64 * wave + lane, a.N - 1) * kbs);
   const uint32_t lo_s = (uint32_t)(64 * wave * 4);
@@ -165,32 +172,40 @@ __global__ __launch_bounds__(256, 1) void k_mx_gemm(MxArgs a) {
                                                                         (int)(a.M * kbs), 0x00020000);
   const __amdgpu_buffer_rsrc_t rw_s = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.w_scales), (short)0,
                                                                         (int)(a.N * kbs), 0x00020000);
-  auto issue = [&](int st, int64_t k0) {
-    uint8_t* base = smem + st * XS_BYTES;
-    const int kc = (int)(k0 >> 1), ks = (int)(k0 >> 5) & ~3;
+  // slot sl <- K steps 4 s .. 4 s + 3 (elements k0 = 256 s ..)
+  auto issue = [&](int sl, int64_t k0) {
+    uint8_t* base = smem + sl * XS_BYTES;
+    const int kc = (int)(k0 >> 1), ks = (int)(k0 >> 5);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      mx_load_lds(ra_c, base + XS_A + lo_c[q], 16, oa_c[q], kc);
-      mx_load_lds(rw_c, base + XS_W + lo_c[q], 16, ow_c[q], kc);
+    for (int q = 0; q < 8; ++q) {
+      mx_load_lds(ra_c, base + XS_A + lo_c + q * 1024, 16, oa_c[q], kc);
+      mx_load_lds(rw_c, base + XS_W + lo_c + q * 1024, 16, ow_c[q], kc);
     }
-    mx_load_lds(ra_s, base + XS_SA + lo_s, 4, oa_s, ks);
-    mx_load_lds(rw_s, base + XS_SW + lo_s, 4, ow_s, ks);
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      mx_load_lds(ra_s, base + XS_SA + d * 1024 + lo_s, 4, oa_s, ks + 4 * d);
+      mx_load_lds(rw_s, base + XS_SW + d * 1024 + lo_s, 4, ow_s, ks + 4 * d);
+    }
   };
 
-  const int swz = (li >> 2 ^ li >> 3) & 1;
-  const uint32_t la_c = (uint32_t)(XS_A + (wm * 128 + li) * 32 + 16 * (h ^ swz));
-  const uint32_t lw_c = (uint32_t)(XS_W + (wn * 128 + li) * 32 + 16 * (h ^ swz));
+  // operand reads: row r = w * 128 + 32 i + li, K step sub of the slot: logical chunk
+  // 2 sub + h at physical chunk (2 sub + h) ^ (li & 7); scale byte 2 (sub & 1) + h of
+  // dword plane sub >> 1
+  const uint32_t la_c = (uint32_t)(XS_A + (wm * 128 + li) * 128);
+  const uint32_t lw_c = (uint32_t)(XS_W + (wn * 128 + li) * 128);
   const uint32_t la_s = (uint32_t)(XS_SA + (wm * 128 + li) * 4 + h);
   const uint32_t lw_s = (uint32_t)(XS_SW + (wn * 128 + li) * 4 + h);
-  // step kt's scale pair is bytes 2 (kt & 1), +1 of the staged dword
-  auto lread = [&](int st, MxRegs& r, int64_t kt) {
-    const uint8_t* base = smem + st * XS_BYTES;
-    const uint8_t* sbase = base + 2 * (int)(kt & 1);
+  const int l7 = li & 7;
+  auto lread = [&](int64_t kt, MxRegs& r) {
+    const int sub = (int)(kt & 3);
+    const uint8_t* base = smem + (int)((kt >> 2) & 1) * XS_BYTES;
+    const uint32_t coff = (uint32_t)(16 * ((2 * sub + h) ^ l7));
+    const uint8_t* sbase = base + (sub >> 1) * 1024 + 2 * (sub & 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      r.a[i] = *reinterpret_cast<const u32x4*>(base + la_c + i * 1024);
+      r.a[i] = *reinterpret_cast<const u32x4*>(base + la_c + coff + i * 4096);
       r.sa[i] = sbase[la_s + i * 128];
-      r.b[i] = *reinterpret_cast<const u32x4*>(base + lw_c + i * 1024);
+      r.b[i] = *reinterpret_cast<const u32x4*>(base + lw_c + coff + i * 4096);
       r.sb[i] = sbase[lw_s + i * 128];
     }
   };
@@ -213,26 +228,30 @@ __global__ __launch_bounds__(256, 1) void k_mx_gemm(MxArgs a) {
 
   MxRegs R0, R1;
   const int64_t nk = K / XBK;           // even (K % 128 == 0)
-  // K step kt with operands in cur; reads step kt+1 into nxt.  The loads of step kt+3
-  // are issued every step: past the last step they re-read it into the ring stage of
-  // step kt-1, which no later step reads, so the in-flight count stays uniform.
+  const int64_t nslot = (nk + XSS - 1) / XSS;
+  // K step kt with operands in cur; reads step kt+1 into nxt.  At the first step of a
+  // slot the loads of the next slot go into the other slot, whose last reads (step
+  // kt-1, read during step kt-2) ended before the barrier of step kt-1.  At the last
+  // step of a slot every wave waits for its loads of the next slot, then the barrier
+  // publishes them; inside a slot no barrier is needed.
   auto kstep = [&](int64_t kt, MxRegs& cur, MxRegs& nxt, bool next) {
-    issue((int)((kt + 3) & 3), min<int64_t>(kt + 3, nk - 1) * XBK);
+    const int64_t sl = kt >> 2;
+    if ((kt & 3) == 0 && sl + 1 < nslot) issue((int)((sl + 1) & 1), (sl + 1) * XSS * XBK);
     mfma_rows(cur, 0);
     if (next) {
-      wait_vmcnt<12>();                 // this wave's loads of step kt+1 have landed
-      wg_barrier();                     // ... and every other wave's
-      lread((int)((kt + 1) & 3), nxt, kt + 1);
+      if (((kt + 1) & 3) == 0) {
+        wait_vmcnt<0>();
+        wg_barrier();
+      }
+      lread(kt + 1, nxt);
     }
     mfma_rows(cur, 2);
   };
 
   issue(0, 0);
-  issue(1, XBK);
-  issue(2, min<int64_t>(2, nk - 1) * XBK);
-  wait_vmcnt<12>();
+  wait_vmcnt<0>();
   wg_barrier();
-  lread(0, R0, 0);
+  lread(0, R0);
   for (int64_t kt = 0; kt < nk; kt += 2) {
     kstep(kt, R0, R1, true);
     kstep(kt + 1, R1, R0, kt + 2 < nk);
