@@ -37,7 +37,8 @@
  *     the null stream).
  *   - Inputs containing NaN or Inf are outside the contract (results unspecified).
  *   - Errors: NVFP4_ERR_INVALID_ARG (null pointer, size <= 0, K % 16 != 0,
- *     ld < K, bad segment table, gate shape mismatch), NVFP4_ERR_UNSUPPORTED
+ *     ld < K, bad segment table, gate shape mismatch, distinct segment scales
+ *     where one scale is required), NVFP4_ERR_UNSUPPORTED
  *     (dtype or alignment outside the supported set), NVFP4_ERR_DEVICE (current
  *     device is not gfx950), NVFP4_ERR_HIP (a HIP launch error).
  *   - Alignment: x, w, y and the packed buffers must be 16-byte aligned, and
@@ -143,7 +144,13 @@ NVFP4_API int32_t nvfp4_w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scale
                         void* y, int32_t y_dtype, int64_t ldy, void* stream);
 
 /*
- * The whole layer in one call: activation quantization + GEMM + epilogues.
+ * The whole layer in one call: activation quantization + GEMM + epilogues, i.e. the
+ * two stages of the layer ("Why Gated DeltaNet Survives 4-Bit Quantization" review
+ * page: background section for the NVFP4 activations, strengths paragraph / the
+ * paper's section 6 for the per-segment scales, mechanism step 2, Eq. 1 for the
+ * gates).  Fusing the activation quantization into the GEMM addresses the
+ * small-batch quantization overhead the page names for decode (limitations, the
+ * paper's section 9).
  * Results equal nvfp4_quantize_act followed by nvfp4_w4a4_gemm.  Decode shapes
  * (M <= 8) and skinny shapes (N <= 128 with K a multiple of 256) run fused
  * kernels that quantize x in registers and never write the activation codes to
@@ -183,7 +190,9 @@ NVFP4_API int32_t nvfp4_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, i
  *   gscale_shared  device, 1 fp32 (finite, > 0), or NULL: the largest segment scale
  *   codes_out, scales_out device outputs [N][K/2], [N][K/16]; may be the same
  *                  buffers as codes, scales (in place), otherwise must not overlap them
- *   gscale_out     device, 1 fp32 (output): the shared scale used
+ *   gscale_out     device, 1 fp32 (output): the shared scale used; must not point
+ *                  into seg_gscale nor equal gscale_shared (NVFP4_ERR_INVALID_ARG),
+ *                  since the kernel writes it while other workgroups read those
  */
 NVFP4_API int32_t nvfp4_requantize_weight(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
                                 int32_t n_seg, const int64_t* seg_end, const float* seg_gscale,
@@ -203,6 +212,19 @@ NVFP4_API int32_t nvfp4_requantize_weight(const uint8_t* codes, const uint8_t* s
  */
 NVFP4_API int32_t nvfp4_segment_mismatch_factor(int32_t n_seg, const float* seg_gscale, float g_used,
                                       double* factor_out, int32_t* worst_out);
+
+/*
+ * Guard for single-scale launches (host only, nothing enqueued): returns NVFP4_OK
+ * when the n_seg segment scales a fused weight was packed with (seg_gscale, host,
+ * finite, > 0) are all equal, so that nvfp4_w4a4_gemm / nvfp4_w4a4_linear may run
+ * it with n_seg == 1 and that one scale; otherwise NVFP4_ERR_INVALID_ARG, with the
+ * offending segment and its ratio in the message.  The GEMM cannot make this check
+ * itself: the segment scales it receives are device memory, and validation never
+ * synchronizes.  The mismatch it catches is silent in the outputs ("Why Gated
+ * DeltaNet Survives 4-Bit Quantization" review page, strengths paragraph / the
+ * paper's section 6).
+ */
+NVFP4_API int32_t nvfp4_require_single_scale(int32_t n_seg, const float* seg_gscale);
 
 /*
  * MXFP4 variant (the format the review page names as the next generalization,

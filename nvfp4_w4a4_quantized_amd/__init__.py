@@ -29,7 +29,7 @@ NVFP4_MAX_SEGMENTS = 64
 
 EXPORTED = ["nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize_act", "nvfp4_pack_weight",
             "nvfp4_w4a4_gemm", "nvfp4_w4a4_linear", "nvfp4_requantize_weight", "nvfp4_segment_mismatch_factor",
-            "nvfp4_mxfp4_quantize", "nvfp4_mxfp4_gemm"]
+            "nvfp4_require_single_scale", "nvfp4_mxfp4_quantize", "nvfp4_mxfp4_gemm"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -64,6 +64,8 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_requantize_weight.argtypes = [P, P, I64, I64, I32, P, P, P, P, P, P, P]
     lib.nvfp4_segment_mismatch_factor.restype = I32
     lib.nvfp4_segment_mismatch_factor.argtypes = [I32, P, ctypes.c_float, P, P]
+    lib.nvfp4_require_single_scale.restype = I32
+    lib.nvfp4_require_single_scale.argtypes = [I32, P]
     lib.nvfp4_mxfp4_quantize.restype = I32
     lib.nvfp4_mxfp4_quantize.argtypes = [P, I32, I64, I64, I64, P, P, P]
     lib.nvfp4_mxfp4_gemm.restype = I32
@@ -208,6 +210,14 @@ def nvfp4_segment_mismatch_factor(seg_gscale: Sequence[float], g_used: float):
     w = ctypes.c_int32(0)
     _check(lib.nvfp4_segment_mismatch_factor(n, arr, ctypes.c_float(g_used), ctypes.byref(f), ctypes.byref(w)))
     return f.value, w.value
+
+
+def nvfp4_require_single_scale(seg_gscale: Sequence[float]) -> None:
+    """Raises Nvfp4Error unless every host segment scale of a fused weight is the
+    same, i.e. unless a single-scale GEMM (one segment) over it is exact."""
+    n = len(seg_gscale)
+    arr = (ctypes.c_float * max(n, 1))(*[float(v) for v in seg_gscale])
+    _check(lib.nvfp4_require_single_scale(n, arr))
 
 
 def empty_mx_packed(rows: int, K: int, device="cuda"):

@@ -330,6 +330,11 @@ int32_t nvfp4_requantize_weight(const uint8_t* codes, const uint8_t* scales, int
   if (st) return st;
   if (!seg_gscale) return fail(NVFP4_ERR_INVALID_ARG, "seg_gscale is NULL");
   if (!gscale_out) return fail(NVFP4_ERR_INVALID_ARG, "gscale_out is NULL");
+  // the kernel writes *gscale_out while other workgroups still read the segment
+  // scales and the shared scale: it must alias neither
+  if (n_seg >= 1 && n_seg <= NVFP4_MAX_SEGMENTS && gscale_out >= seg_gscale && gscale_out < seg_gscale + n_seg)
+    return fail(NVFP4_ERR_INVALID_ARG, "gscale_out must not point into seg_gscale");
+  if (gscale_out == gscale_shared) return fail(NVFP4_ERR_INVALID_ARG, "gscale_out must not alias gscale_shared");
   // in place, or no overlap at all (a partial overlap would let one lane read bytes
   // that another has already rewritten)
   const uintptr_t cb = (uintptr_t)codes, co = (uintptr_t)codes_out, sb = (uintptr_t)scales, so = (uintptr_t)scales_out;
@@ -369,6 +374,20 @@ int32_t nvfp4_segment_mismatch_factor(int32_t n_seg, const float* seg_gscale, fl
   }
   if (factor_out) *factor_out = worst;
   if (worst_out) *worst_out = at;
+  return ok();
+}
+
+int32_t nvfp4_require_single_scale(int32_t n_seg, const float* seg_gscale) {
+  double factor = 0.0;
+  int32_t worst = 0;
+  const int32_t st = nvfp4_segment_mismatch_factor(n_seg, seg_gscale, n_seg >= 1 && seg_gscale ? seg_gscale[0] : 1.0f,
+                                                   &factor, &worst);
+  if (st) return st;
+  if (factor != 1.0)
+    return fail(NVFP4_ERR_INVALID_ARG,
+                "the weight has more than one distinct segment scale (segment %d is %.6g times segment 0's): a "
+                "GEMM launched with n_seg == 1 would mis-scale it; pass its segment table",
+                worst, (double)seg_gscale[worst] / (double)seg_gscale[0]);
   return ok();
 }
 

@@ -658,14 +658,8 @@ size_t gemv_lds_bytes(int64_t M, int64_t K) { return (size_t)M * (size_t)K * 2; 
 template <InType T, int NL>
 static hipError_t launch_stream(const GemvArgs& p, unsigned grid, size_t lds, hipStream_t s) {
   constexpr int NA = NVFP4_GEMV_AHEAD(NL);
-  // allow dynamic LDS beyond the 64 KiB default (set once per instantiation)
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_stream<T, NL, NA>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 152 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = lds_limit_once<&k_gemv_stream<T, NL, NA>>(152 * 1024);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gemv_stream<T, NL, NA>), dim3(grid), dim3(GS_THREADS), lds, s, p);
   return hipGetLastError();
 }
@@ -680,13 +674,8 @@ static hipError_t launch_stream(const GemvArgs& p, unsigned grid, size_t lds, hi
 template <InType T, int NL>
 static hipError_t launch_ws(const GemvArgs& p, unsigned grid, size_t lds, hipStream_t s) {
   constexpr int NA = NVFP4_GEMV_WS_AHEAD(NL);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ws<T, NL, NA>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, GW_LDS_MAX);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = lds_limit_once<&k_gemv_ws<T, NL, NA>>(GW_LDS_MAX);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gemv_ws<T, NL, NA>), dim3(grid), dim3(GW_THREADS), lds, s, p);
   return hipGetLastError();
 }

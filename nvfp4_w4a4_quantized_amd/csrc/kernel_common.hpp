@@ -19,7 +19,13 @@ __device__ __forceinline__ float softplus_f32(float z) {
   return __builtin_fmaxf(z, 0.0f) + log1pf(expf(-__builtin_fabsf(z)));
 }
 
-__device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + expf(-z)); }
+// 1/(1+e^-z), evaluated as e^z/(1+e^z) for z < 0 so that e^-z never overflows: for
+// z below about -87.3 the result is an fp32 subnormal rather than 0.
+__device__ __forceinline__ float sigmoid_f32(float z) {
+  const float e = expf(-__builtin_fabsf(z));
+  const float r = 1.0f / (1.0f + e);
+  return z >= 0.0f ? r : e * r;
+}
 
 // Workgroup barrier that waits for this wave's LDS traffic only.  __syncthreads()
 // would also wait for every outstanding global load (vmcnt(0)); kernels that keep a
@@ -83,6 +89,17 @@ __device__ __forceinline__ f16x2 bcast(f16x2 p, int hi) {
   f16x2 r;
   if (hi) { r[0] = p[1]; r[1] = p[1]; } else { r[0] = p[0]; r[1] = p[0]; }
   return r;
+}
+
+// Raise a kernel's dynamic-LDS limit beyond the 64 KiB default, once per process:
+// a function-local static is initialised exactly once even when several host
+// threads make their first call together (C++11), and every later call returns the
+// status of that one hipFuncSetAttribute.
+template <auto Kernel>
+hipError_t lds_limit_once(int bytes) {
+  static const hipError_t e =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  return e;
 }
 
 #define SCHED_MFMA_VALU(n_mfma, n_valu)                          \

@@ -239,14 +239,9 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_linear_skinny(GemvArgs p) {
 
 template <InType T, int NT, int EPI, bool CODES>
 hipError_t launch_ntc(const GemvArgs& p, hipStream_t s) {
-  static bool attr_set = false;
   const size_t lds = 2 * (size_t)NT * 16 * SK_ROWB;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_linear_skinny<T, NT, EPI, CODES>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = lds_limit_once<&k_linear_skinny<T, NT, EPI, CODES>>((int)lds);
+  if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((p.g.M + SK_TM - 1) / SK_TM);
   hipLaunchKernelGGL((k_linear_skinny<T, NT, EPI, CODES>), dim3(grid), dim3(SK_THREADS), lds, s, p);
   return hipGetLastError();

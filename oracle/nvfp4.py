@@ -134,20 +134,6 @@ def e2m1_rne_sat(r):
 
 
 # ----------------------------------------------------------------------------
-# Input conversion
-# ----------------------------------------------------------------------------
-
-def bf16_bits_to_f64(bits):
-    """Exact float64 value of bf16 bit patterns (uint16)."""
-    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
-    return b.view(np.float32).astype(np.float64)
-
-
-def f32_to_f64(x):
-    return np.asarray(x, dtype=np.float32).astype(np.float64)
-
-
-# ----------------------------------------------------------------------------
 # Global scale (R3)
 # ----------------------------------------------------------------------------
 
@@ -349,6 +335,7 @@ def linear_reference(a_codes, a_scales, a_g, w_codes, w_scales, seg_end, w_g_seg
 # ----------------------------------------------------------------------------
 
 U32 = 2.0 ** -24
+F32_TINY = 2.0 ** -149          # smallest fp32 subnormal
 
 
 def ulp(y, out_dtype):
@@ -379,9 +366,14 @@ def gemm_elem_bound(y64, abs_prod, alpha_cols, K, out_dtype):
 
 def gate_elem_bound(y64_gemm, gemm_bound, A_log, dt_bias, out_rounded):
     """Per-element bound for the gate outputs [g | beta] (fp32):
-    |dg| <= e^A_log * sigmoid(z) * (E_a + u(|y| + |dt_bias|)) + 8u|g| + ulp(g),
-    |dbeta| <= beta(1-beta) * E_b + 8u*beta + ulp(beta).
-    The u(|y|+|dt_bias|) term covers the fp32 rounding of z = y + dt_bias."""
+    |dg| <= e^A_log * sigmoid(z) * (E_a + u(|y| + |dt_bias|)) + 8u|g| + ulp(g)
+            + (1 + e^A_log) * 2^-149,
+    |dbeta| <= beta(1-beta) * E_b + 8u*beta + ulp(beta) + 2 * 2^-149.
+    The u(|y|+|dt_bias|) term covers the fp32 rounding of z = y + dt_bias; 8u
+    covers the relative error of the fp32 exp/log1p/divide; the 2^-149 terms
+    cover results in the fp32 subnormal range (z below about -87), where each
+    fp32 rounding costs up to half a subnormal spacing in absolute terms and
+    the one of softplus is then multiplied by e^A_log."""
     A_log = np.asarray(A_log, dtype=np.float32).astype(np.float64)
     dt_bias = np.asarray(dt_bias, dtype=np.float32).astype(np.float64)
     H = A_log.shape[0]
@@ -391,8 +383,8 @@ def gate_elem_bound(y64_gemm, gemm_bound, A_log, dt_bias, out_rounded):
     g = -np.exp(A_log)[None, :] * softplus_f64(z)
     beta = sigmoid_f64(yb)
     bg = np.exp(A_log)[None, :] * sig_z * (gemm_bound[:, :H] + U32 * (np.abs(ya) + np.abs(dt_bias)[None, :])) \
-        + 8 * U32 * np.abs(g) + ulp(out_rounded[:, :H], "f32")
-    bb = beta * (1 - beta) * gemm_bound[:, H:] + 8 * U32 * beta + ulp(out_rounded[:, H:], "f32")
+        + 8 * U32 * np.abs(g) + ulp(out_rounded[:, :H], "f32") + (1.0 + np.exp(A_log))[None, :] * F32_TINY
+    bb = beta * (1 - beta) * gemm_bound[:, H:] + 8 * U32 * beta + ulp(out_rounded[:, H:], "f32") + 2 * F32_TINY
     return np.concatenate([bg, bb], axis=1)
 
 

@@ -123,7 +123,8 @@ def test_binding_rejects_wrong_dtype(nv):
 
 
 def test_requantize_weight_validation(nv):
-    def call(N=96, K=64, seg_vals=(48, 96), codes=FAKE, scales=FAKE, sg=FAKE, co=None, so=None, gout=FAKE):
+    def call(N=96, K=64, seg_vals=(48, 96), codes=FAKE, scales=FAKE, sg=FAKE, co=None, so=None,
+             gout=ctypes.c_void_p(1 << 23)):
         seg, n = _segs(list(seg_vals))
         co = ctypes.c_void_p((1 << 24)) if co is None else co
         so = ctypes.c_void_p((1 << 25)) if so is None else so
@@ -138,6 +139,14 @@ def test_requantize_weight_validation(nv):
     # output codes starting 16 bytes into the input codes: a partial overlap
     assert call(co=ctypes.c_void_p(FAKE.value + 16)) == nv.NVFP4_ERR_INVALID_ARG and "overlap" in nv.nvfp4_last_error()
     assert call(so=ctypes.c_void_p(FAKE.value + 16)) == nv.NVFP4_ERR_INVALID_ARG and "overlap" in nv.nvfp4_last_error()
+    # the shared scale written over a segment scale that other workgroups still read
+    sg = ctypes.c_void_p(1 << 26)
+    assert call(sg=sg, gout=sg) == nv.NVFP4_ERR_INVALID_ARG and "seg_gscale" in nv.nvfp4_last_error()
+    assert call(sg=sg, gout=ctypes.c_void_p(sg.value + 4)) == nv.NVFP4_ERR_INVALID_ARG
+    seg, n = _segs([48, 96])
+    assert nv.lib.nvfp4_requantize_weight(FAKE, FAKE, 96, 64, n, seg, sg, FAKE, ctypes.c_void_p(1 << 24),
+                                          ctypes.c_void_p(1 << 25), FAKE, None) == nv.NVFP4_ERR_INVALID_ARG
+    assert "gscale_shared" in nv.nvfp4_last_error()
 
 
 def test_segment_mismatch_factor_matches_oracle(nv):
@@ -157,6 +166,22 @@ def test_segment_mismatch_factor_matches_oracle(nv):
         nv.nvfp4_segment_mismatch_factor([1.0], 0.0)
     with pytest.raises(nv.Nvfp4Error):
         nv.nvfp4_segment_mismatch_factor([1.0] * 65, 1.0)
+
+
+def test_single_scale_guard(nv):
+    """A single-scale launch over a fused weight whose segments were packed with
+    different global scales is refused by the host guard; equal scales pass."""
+    nv.nvfp4_require_single_scale([0.5])
+    nv.nvfp4_require_single_scale([2.0e-5] * 4)
+    for scales in ([1.5e-5, 6.0e-5], [1.0, 1.0, 1.0000001], [3.0, 3.0, 0.75, 3.0]):
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_require_single_scale(scales)
+        assert e.value.status == nv.NVFP4_ERR_INVALID_ARG and "more than one distinct" in str(e.value)
+    with pytest.raises(nv.Nvfp4Error):
+        nv.nvfp4_require_single_scale([])
+    with pytest.raises(nv.Nvfp4Error):
+        nv.nvfp4_require_single_scale([1.0, float("nan")])
+    assert nv.lib.nvfp4_require_single_scale(2, None) == nv.NVFP4_ERR_INVALID_ARG
 
 
 def test_mxfp4_validation(nv):

@@ -507,3 +507,50 @@ def test_linear_skinny_equals_two_stage(nv):
     assert torch.equal(ac1, ac2) and torch.equal(as1, as2)
     a, b = y1.double(), y2.double()
     assert float(torch.linalg.norm(a - b) / torch.linalg.norm(b)) < 1e-5
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_full_gdn_gates_fused_linear_sampled(nv, mode):
+    """The GDN gate projections at full size (32768 x 96 x 5120) through
+    nvfp4_w4a4_linear, i.e. the fused skinny kernel in the launch configuration the
+    benchmark times (static: a calibrated scale equal to this tensor's amax-derived
+    one, no codes written), and again with the activation codes requested (and in
+    dynamic mode).  One sampled token from every 128-token workgroup range plus the
+    last token: codes, scale bytes and the global scale bit-exact, outputs within the
+    gate bound (Eq. 1 of the review page, mechanism step 2)."""
+    name = "gdn_gates_32768x96x5120"
+    wl = W.generate(name)
+    xv, xt = _x_inputs(wl)
+    w = wl.data["w32"]
+    wc, ws, wg = P.gpu_pack(nv, P.dev_x(w), wl.seg_end, None)
+    M, N, K = wl.M, wl.N, wl.K
+    gate = (torch.from_numpy(wl.data["A_log"]).cuda(), torch.from_numpy(wl.data["dt_bias"]).cuda())
+    ag = O.global_scale(O.tensor_amax(P.x64_of(xv)))
+    gin = torch.tensor([float(ag)], dtype=torch.float32, device="cuda") if mode == "static" else None
+    outs = []
+    for with_codes in ((False, True) if mode == "static" else (True,)):
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        gout = torch.empty(1, dtype=torch.float32, device="cuda")
+        ac = as_ = None
+        if with_codes:
+            ac, as_ = nv.empty_packed(M, K, "cuda")
+        nv.nvfp4_w4a4_linear(xt, gin, gout, wc, ws, wl.seg_end, wg, y, gate=gate, a_codes_out=ac, a_scales_out=as_)
+        torch.cuda.synchronize()
+        assert np.float32(gout.item()) == ag
+        outs.append((y, ac, as_))
+    rng = np.random.default_rng(17)
+    rows = np.arange(0, M, 128) + rng.integers(0, 128, M // 128)
+    rows = np.unique(np.append(rows, M - 1))
+    rsel = torch.from_numpy(rows).cuda()
+    oac, oas = O.quantize_rows(P.x64_of(xv[rows]), np.full(len(rows), ag, dtype=np.float32))
+    owc, ows, owg = O.pack_weight(w.astype(np.float64), wl.seg_end)
+    assert np.array_equal(owg, wg.cpu().numpy())
+    yref, _, bound = P.oracle_reference(oac, oas, ag, owc, ows, wl.seg_end, owg, "f32",
+                                        gate=(wl.data["A_log"], wl.data["dt_bias"]))
+    for y, ac, as_ in outs:
+        if ac is not None:
+            P.assert_bytes_equal(ac[rsel].cpu().numpy(), oac, "activation codes (sampled)")
+            P.assert_bytes_equal(as_[rsel].cpu().numpy(), oas, "activation scales (sampled)")
+        P.assert_within_tolerance(P.y_to_f64(y[rsel]), yref, bound, f"gates fused {mode}")
+    if len(outs) == 2:
+        assert torch.equal(outs[0][0], outs[1][0])      # writing the codes does not change y

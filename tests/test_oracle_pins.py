@@ -406,6 +406,105 @@ def test_error_bound_admits_fp32_gemm_and_rejects_planted_error():
     assert np.any(np.abs(planted - yref) > bound)
 
 
+def _seq_fp32_acc(a_s, w_s):
+    """fp32 accumulation in plain k order (one rounding per partial sum)."""
+    acc = np.zeros((a_s.shape[0], w_s.shape[0]), np.float32)
+    for k in range(a_s.shape[1]):
+        acc = acc + np.outer(a_s[:, k], w_s[:, k]).astype(np.float32)
+    return acc
+
+
+def _to_bf16_f64(y32):
+    """fp32 -> bf16 by torch's own RNE cast (independent of the oracle), as float64."""
+    return torch.from_numpy(np.ascontiguousarray(y32, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def test_error_bound_bf16_output_admits_fp32_gemm_and_is_tight():
+    # bf16-output branch of the per-element bound: an fp32 GEMM (exact scale-decoded
+    # operands, fp32 sums in BLAS order and in plain k order, fp32 alpha and multiply)
+    # rounded to bf16 by torch lies within it; a planted 2-ulp bf16 error is flagged at
+    # most elements (a bound 10x too loose would flag none)
+    wl = W.generate("gdn_in_proj_8192x16384x5120", M=32, with_weight=False)
+    x = W.x_values_f32(wl).astype(np.float64)
+    rng = np.random.default_rng(7)
+    N = 192
+    w = (rng.standard_normal((N, wl.K)) * 0.02).astype(np.float32).astype(np.float64)
+    ac, as_, ag = O.quantize_activation(x)
+    wc, ws, gw = O.pack_weight(w, [N])
+    yref, y64 = O.linear_reference(ac, as_, ag, wc, ws, [N], gw, "bf16")
+    a_s = O.dequantize_rows(ac, as_).astype(np.float32)
+    w_s = O.dequantize_rows(wc, ws).astype(np.float32)
+    alpha = np.float32(ag) * np.float32(gw[0])
+    bound = O.gemm_elem_bound(y64, O.gemm_abs_product(ac, as_, wc, ws), np.full(N, alpha, np.float64), wl.K, "bf16")
+    for acc in (a_s @ w_s.T, _seq_fp32_acc(a_s, w_s)):
+        yb = _to_bf16_f64((acc * alpha).astype(np.float32))
+        assert np.all(np.abs(yb - yref) <= bound)
+        # bf16 spacing at each reference value, from torch's bf16 grid
+        up = torch.from_numpy(yref.astype(np.float32)).to(torch.bfloat16)
+        ulp = (torch.nextafter(up, torch.full_like(up, float("inf"))) - up).double().abs().numpy()
+        planted = yb + 2 * ulp
+        assert np.mean(np.abs(planted - yref) > bound) >= 0.25
+    assert np.median(bound / ulp) < 3.0
+
+
+def test_gate_bound_admits_fp32_epilogue_and_rejects_planted_errors():
+    # the gate outputs' bound against an fp32 emulation of the GPU epilogue: fp32 GEMM
+    # sums, y = acc * alpha in fp32, z = y + dt_bias in fp32, numpy's float32
+    # exp/log1p, g = -exp(A_log) * softplus(z), beta = 1/(1+e^-y) evaluated without
+    # overflow.  Adversarial parameters: A_log at 0 and 2.7, dt_bias from -100 to 100 and
+    # near 0, head weights from 0.002 to 0.5 so that y spans tiny to +-100 (subnormal
+    # outputs included).  Planted errors of 1e-3 relative in g and in beta are flagged,
+    # and so is a sigmoid that overflows e^-y to give 0 for y < -88.
+    wl = W.generate("gdn_gates_32768x96x5120", M=64)
+    x = W.x_values_f32(wl).astype(np.float64)
+    H = 48
+    rng = np.random.default_rng(11)
+    A_log = np.linspace(0.0, 2.7, H).astype(np.float32)
+    dt = np.concatenate([np.linspace(-100, 100, 24), rng.standard_normal(24) * 0.01]).astype(np.float32)
+    sig = np.concatenate([np.geomspace(0.002, 0.2, 48), np.geomspace(0.002, 0.5, 48)])
+    w = (rng.standard_normal((96, wl.K)) * sig[:, None]).astype(np.float32).astype(np.float64)
+    ac, as_, ag = O.quantize_activation(x)
+    wc, ws, gw = O.pack_weight(w, [48, 96])
+    y64 = O.gemm_f64(ac, as_, ag, wc, ws, [48, 96], gw)
+    out64 = O.gate_epilogue_f64(y64, A_log, dt)
+    yref = O.round_output(out64, "f32")
+    alpha = (np.float32(ag) * gw[np.repeat([0, 1], 48)]).astype(np.float32)
+    gb = O.gemm_elem_bound(y64, O.gemm_abs_product(ac, as_, wc, ws), alpha.astype(np.float64), wl.K, "f32")
+    bound = O.gate_elem_bound(y64, gb, A_log, dt, yref)
+    a_s = O.dequantize_rows(ac, as_).astype(np.float32)
+    w_s = O.dequantize_rows(wc, ws).astype(np.float32)
+    f32 = np.float32
+
+    def epilogue(acc, stable_sigmoid=True):
+        y = (acc * alpha[None, :]).astype(f32)
+        z = (y[:, :H] + dt[None, :]).astype(f32)
+        with np.errstate(over="ignore"):
+            sp = (np.maximum(z, f32(0)) + np.log1p(np.exp(-np.abs(z)))).astype(f32)
+            g = (-np.exp(A_log)[None, :] * sp).astype(f32)
+            yb = y[:, H:]
+            if stable_sigmoid:
+                e = np.exp(-np.abs(yb))
+                r = f32(1) / (f32(1) + e)
+                beta = np.where(yb >= 0, r, e * r).astype(f32)
+            else:
+                beta = (f32(1) / (f32(1) + np.exp(-yb))).astype(f32)
+        return np.concatenate([g, beta], axis=1).astype(np.float64), y
+
+    for acc in (a_s @ w_s.T, _seq_fp32_acc(a_s, w_s)):
+        emu, y = epilogue(acc)
+        assert np.all(np.abs(emu - yref) <= bound)
+    # the inputs reach the extremes they are meant to
+    assert y[:, :H].min() + dt.min() < -87 and y[:, :H].max() + dt.max() > 87
+    assert y[:, H:].min() < -88 and np.any((yref[:, H:] > 0) & (yref[:, H:] < 2.0 ** -126))
+    for sl in (slice(0, H), slice(H, 2 * H)):
+        planted = emu.copy()
+        planted[:, sl] *= 1.0 + 1e-3
+        flagged = np.abs(planted[:, sl] - yref[:, sl]) > bound[:, sl]
+        assert np.mean(flagged) >= 0.1, np.mean(flagged)
+    overflowing, _ = epilogue(a_s @ w_s.T, stable_sigmoid=False)
+    assert np.any(np.abs(overflowing - yref) > bound)
+
+
 # --------------------------------------------------------------------------- shared-scale re-encoding
 
 def _xhat_rows(codes, scales, g_rows):
