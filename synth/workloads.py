@@ -146,3 +146,35 @@ def random_rows(n_rows: int, k: int, seed: int, dtype: str = "bf16", scale: floa
         b = _to_bf16_bits(x)
         return bf16_bits_to_f32(b), b
     return x, None
+
+
+# --------------------------------------------------------------------------- GDN recurrence inputs
+
+GDN_HEADS = dict(n_k_heads=16, n_v_heads=48, d_k=128, d_v=128)
+
+
+def gdn_recurrence_inputs(T: int, n_k_heads: int = 16, n_v_heads: int = 48, d_k: int = 128, d_v: int = 128,
+                          seed: int = 0, with_state: bool = False) -> dict:
+    """Seeded inputs of the gated delta-rule recurrence (fp32 arrays).
+
+    Recipe: keys and queries N(0, 1) per head, divided by their L2 norm (unit vectors,
+    computed in float64 and stored as fp32); values N(0, 1); the gate output row
+    [g | beta] with g = -10^U(-5, 1.3) (decays from alpha ~ 0.99999, the long
+    horizons of a trained model, to alpha ~ e^-20) and beta ~ U(0.02, 0.98); an
+    initial state N(0, 0.1) when asked.  Draw order: q, k, v, g, beta, state.
+    """
+    rng = np.random.default_rng(seed)
+
+    def unit(shape):
+        a = rng.standard_normal(shape)
+        return (a / np.linalg.norm(a, axis=-1, keepdims=True)).astype(np.float32)
+
+    q = unit((T, n_k_heads, d_k))
+    k = unit((T, n_k_heads, d_k))
+    v = rng.standard_normal((T, n_v_heads, d_v), dtype=np.float32)
+    g = (-(10.0 ** rng.uniform(-5.0, 1.3, (T, n_v_heads)))).astype(np.float32)
+    beta = rng.uniform(0.02, 0.98, (T, n_v_heads)).astype(np.float32)
+    out = dict(q=q, k=k, v=v, gates=np.concatenate([g, beta], axis=1))
+    if with_state:
+        out["state0"] = (rng.standard_normal((n_v_heads, d_k, d_v)) * 0.1).astype(np.float32)
+    return out
