@@ -172,6 +172,27 @@ NVFP4_API int32_t nvfp4_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, i
                           uint8_t* a_codes_out, uint8_t* a_scales_out, void* stream);
 
 /*
+ * nvfp4_w4a4_linear for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments without a_codes_out/a_scales_out, the same kernels and results.  The
+ * shapes that run in two stages keep their quantized activations in the library's
+ * one fixed device workspace of NVFP4_NOALLOC_WORKSPACE_BYTES, which each GPU holds
+ * from the first such call until the process ends; they need
+ * ceil(M*K/2 / 256)*256 + M*K/16 bytes of it, and a larger shape returns
+ * NVFP4_ERR_INVALID_ARG before anything is enqueued (the fused decode and skinny
+ * shapes use no workspace and have no such limit).  The call allocates and frees
+ * nothing.  Calls that overlap on one GPU (on different streams, or from different
+ * threads) share the workspace and race: serialize them.
+ */
+#define NVFP4_NOALLOC_WORKSPACE_BYTES (32ll << 20)
+NVFP4_API int32_t nvfp4_w4a4_linear_noalloc(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                  const float* gscale_in, float* gscale_out,
+                                  int64_t N, const uint8_t* w_codes, const uint8_t* w_scales,
+                                  int32_t n_seg, const int64_t* seg_end, const float* w_seg_gscale,
+                                  const nvfp4_gate_params* gate,
+                                  void* y, int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
  * Re-encoding of a fused weight onto one shared global scale: the alternative
  * repair of the fused-GEMM global-scale mismatch, where the per-segment epilogue
  * of nvfp4_w4a4_gemm is the other ("Why Gated DeltaNet Survives 4-Bit

@@ -28,7 +28,7 @@ NVFP4_DTYPE_BF16 = 1
 NVFP4_MAX_SEGMENTS = 64
 
 EXPORTED = ["nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize_act", "nvfp4_pack_weight",
-            "nvfp4_w4a4_gemm", "nvfp4_w4a4_linear", "nvfp4_requantize_weight", "nvfp4_segment_mismatch_factor",
+            "nvfp4_w4a4_gemm", "nvfp4_w4a4_linear", "nvfp4_w4a4_linear_noalloc", "nvfp4_requantize_weight", "nvfp4_segment_mismatch_factor",
             "nvfp4_require_single_scale", "nvfp4_mxfp4_quantize", "nvfp4_mxfp4_gemm"]
 
 
@@ -60,6 +60,8 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_w4a4_gemm.argtypes = [P, P, P, I64, I64, I64, P, P, I32, P, P, P, P, I32, I64, P]
     lib.nvfp4_w4a4_linear.restype = I32
     lib.nvfp4_w4a4_linear.argtypes = [P, I32, I64, I64, I64, P, P, I64, P, P, I32, P, P, P, P, I32, I64, P, P, P]
+    lib.nvfp4_w4a4_linear_noalloc.restype = I32
+    lib.nvfp4_w4a4_linear_noalloc.argtypes = [P, I32, I64, I64, I64, P, P, I64, P, P, I32, P, P, P, P, I32, I64, P]
     lib.nvfp4_requantize_weight.restype = I32
     lib.nvfp4_requantize_weight.argtypes = [P, P, I64, I64, I32, P, P, P, P, P, P, P]
     lib.nvfp4_segment_mismatch_factor.restype = I32
@@ -187,6 +189,21 @@ def nvfp4_w4a4_linear(x, gscale_in, gscale_out, w_codes, w_scales, seg_end, w_se
                                  N, w_codes.data_ptr(), w_scales.data_ptr(), n_seg, seg, w_seg_gscale.data_ptr(),
                                  ctypes.byref(g) if g is not None else None, y.data_ptr(), _dtype_code(y), ldy,
                                  _ptr(a_codes_out), _ptr(a_scales_out), _stream(stream)))
+
+
+def nvfp4_w4a4_linear_noalloc(x, gscale_in, gscale_out, w_codes, w_scales, seg_end, w_seg_gscale, y, gate=None,
+                              stream=None) -> None:
+    """The whole layer with no caller workspace: two-stage shapes keep their
+    quantized activations in the library's fixed device workspace."""
+    M, K, ldx = _rows(x, "x")
+    N = w_codes.shape[0]
+    _, _, ldy = _rows(y, "y")
+    seg, n_seg = _seg_array(seg_end)
+    g = _gate(gate)
+    _check(lib.nvfp4_w4a4_linear_noalloc(x.data_ptr(), _dtype_code(x), M, K, ldx, _ptr(gscale_in),
+                                         gscale_out.data_ptr(), N, w_codes.data_ptr(), w_scales.data_ptr(), n_seg,
+                                         seg, w_seg_gscale.data_ptr(), ctypes.byref(g) if g is not None else None,
+                                         y.data_ptr(), _dtype_code(y), ldy, _stream(stream)))
 
 
 def nvfp4_requantize_weight(codes, scales, seg_end, seg_gscale, gscale_shared, codes_out, scales_out, gscale_out,

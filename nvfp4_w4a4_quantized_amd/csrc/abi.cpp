@@ -176,10 +176,67 @@ hipError_t enqueue_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t 
 constexpr int64_t kGemvMaxM = 8;
 constexpr int64_t kGemvLdsBudget = 56 * 1024;
 
-bool gemv_fits(int64_t M, int64_t K, int32_t x_dtype) {
+bool linear_fused_gemv(int64_t M, int64_t K, int32_t x_dtype) {
   if (nvfp4::gemv_stream_fits(M, K, in_type(x_dtype))) return true;
   return M <= kGemvMaxM && K % 128 == 0 && M * K * 2 <= kGemvLdsBudget;
 }
+
+// Whether nvfp4_w4a4_linear runs this shape in one fused kernel (no activation
+// codes in memory) rather than in two stages.
+bool linear_fused(int64_t M, int64_t N, int64_t K, int32_t x_dtype) {
+  return linear_fused_gemv(M, K, x_dtype) || nvfp4::linear_skinny_fits(M, N, K);
+}
+
+// The whole layer.  ws_codes/ws_scales: where the two-stage shapes keep the
+// quantized activations (the caller's a_codes_out/a_scales_out, or the fixed
+// workspace); codes_out/scales_out: the caller's optional copy on the fused paths.
+int32_t linear_impl(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, const float* gscale_in,
+                    float* gscale_out, nvfp4::GemmArgs g, uint8_t* codes_out, uint8_t* scales_out,
+                    uint8_t* ws_codes, uint8_t* ws_scales, hipStream_t s) {
+  if (linear_fused_gemv(M, K, x_dtype)) {
+    nvfp4::GemvArgs p{};
+    p.x = x;
+    p.x_type = in_type(x_dtype);
+    p.ldx = ldx;
+    p.gscale_in = gscale_in;
+    p.gscale_out = gscale_out;
+    p.a_codes_out = codes_out;
+    p.a_scales_out = scales_out;
+    p.g = g;
+    return hip_status(nvfp4::launch_gemv_fused(p, s), "nvfp4_w4a4_linear (fused decode) launch");
+  }
+  if (nvfp4::linear_skinny_fits(M, g.N, K)) {
+    hipError_t e = hipSuccess;
+    const float* g_used = gscale_in;
+    if (!gscale_in) {                      // dynamic mode: amax pass over x first
+      e = nvfp4::launch_fill(gscale_out, 1, nullptr, s);
+      if (e == hipSuccess) e = nvfp4::launch_amax_gscale(x, in_type(x_dtype), M, K, ldx, gscale_out, s);
+      if (e != hipSuccess) return hip_status(e, "nvfp4_w4a4_linear amax launch");
+      g_used = gscale_out;
+    }
+    nvfp4::GemvArgs p{};
+    p.x = x;
+    p.x_type = in_type(x_dtype);
+    p.ldx = ldx;
+    p.gscale_in = g_used;
+    p.gscale_out = gscale_in ? gscale_out : nullptr;
+    p.a_codes_out = codes_out;
+    p.a_scales_out = scales_out;
+    p.g = g;
+    return hip_status(nvfp4::launch_linear_skinny(p, s), "nvfp4_w4a4_linear (fused skinny) launch");
+  }
+  hipError_t e = enqueue_quant_act(x, x_dtype, M, K, ldx, gscale_in, ws_codes, ws_scales, gscale_out, s);
+  if (e != hipSuccess) return hip_status(e, "nvfp4_w4a4_linear quantize launch");
+  g.a_codes = ws_codes;
+  g.a_scales = ws_scales;
+  g.a_gscale = gscale_out;
+  return hip_status(nvfp4::launch_gemm_tiled(g, s), "nvfp4_w4a4_linear gemm launch");
+}
+
+// Offset of the scale bytes in the fixed workspace, and the bytes a two-stage
+// shape needs there.
+int64_t noalloc_scales_offset(int64_t M, int64_t K) { return ((M * (K / 2)) + 255) / 256 * 256; }
+int64_t noalloc_bytes(int64_t M, int64_t K) { return noalloc_scales_offset(M, K) + M * (K / 16); }
 
 }  // namespace
 
@@ -269,53 +326,44 @@ int32_t nvfp4_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, 
   nvfp4::GemmArgs g{};
   st = check_gemm_common(M, N, K, w_codes, w_scales, n_seg, seg_end, w_seg_gscale, gate, y, y_dtype, ldy, &g);
   if (st) return st;
-  const bool fused_gemv = gemv_fits(M, K, x_dtype);
-  const bool fused_skinny = !fused_gemv && nvfp4::linear_skinny_fits(M, N, K);
-  if (!fused_gemv && !fused_skinny && !a_codes_out)
+  if (!linear_fused(M, N, K, x_dtype) && !a_codes_out)
     return fail(NVFP4_ERR_INVALID_ARG,
                 "this shape (M=%lld, N=%lld, K=%lld) runs in two stages and needs a_codes_out/a_scales_out",
                 (long long)M, (long long)N, (long long)K);
   st = check_device();
   if (st) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (fused_gemv) {
-    nvfp4::GemvArgs p{};
-    p.x = x;
-    p.x_type = in_type(x_dtype);
-    p.ldx = ldx;
-    p.gscale_in = gscale_in;
-    p.gscale_out = gscale_out;
-    p.a_codes_out = a_codes_out;
-    p.a_scales_out = a_scales_out;
-    p.g = g;
-    return hip_status(nvfp4::launch_gemv_fused(p, s), "nvfp4_w4a4_linear (fused decode) launch");
+  return linear_impl(x, x_dtype, M, K, ldx, gscale_in, gscale_out, g, a_codes_out, a_scales_out, a_codes_out,
+                     a_scales_out, static_cast<hipStream_t>(stream));
+}
+
+int32_t nvfp4_w4a4_linear_noalloc(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                  const float* gscale_in, float* gscale_out, int64_t N, const uint8_t* w_codes,
+                                  const uint8_t* w_scales, int32_t n_seg, const int64_t* seg_end,
+                                  const float* w_seg_gscale, const nvfp4_gate_params* gate, void* y,
+                                  int32_t y_dtype, int64_t ldy, void* stream) {
+  int32_t st = check_x(x, x_dtype, M, K, ldx, "x");
+  if (st) return st;
+  if (!gscale_out) return fail(NVFP4_ERR_INVALID_ARG, "gscale_out is NULL");
+  nvfp4::GemmArgs g{};
+  st = check_gemm_common(M, N, K, w_codes, w_scales, n_seg, seg_end, w_seg_gscale, gate, y, y_dtype, ldy, &g);
+  if (st) return st;
+  const bool fused = linear_fused(M, N, K, x_dtype);
+  if (!fused && noalloc_bytes(M, K) > nvfp4::kNoallocScratchBytes)
+    return fail(NVFP4_ERR_INVALID_ARG,
+                "M=%lld, K=%lld needs %lld bytes of activation workspace; the fixed workspace holds %lld "
+                "(use nvfp4_w4a4_linear with caller buffers)",
+                (long long)M, (long long)K, (long long)noalloc_bytes(M, K), (long long)nvfp4::kNoallocScratchBytes);
+  st = check_device();
+  if (st) return st;
+  uint8_t* ws = nullptr;
+  if (!fused) {
+    void* p = nullptr;
+    const hipError_t e = nvfp4::noalloc_scratch(&p);
+    if (e != hipSuccess) return hip_status(e, "nvfp4_w4a4_linear_noalloc workspace lookup");
+    ws = static_cast<uint8_t*>(p);
   }
-  if (fused_skinny) {
-    hipError_t e = hipSuccess;
-    const float* g_used = gscale_in;
-    if (!gscale_in) {                      // dynamic mode: amax pass over x first
-      e = nvfp4::launch_fill(gscale_out, 1, nullptr, s);
-      if (e == hipSuccess) e = nvfp4::launch_amax_gscale(x, in_type(x_dtype), M, K, ldx, gscale_out, s);
-      if (e != hipSuccess) return hip_status(e, "nvfp4_w4a4_linear amax launch");
-      g_used = gscale_out;
-    }
-    nvfp4::GemvArgs p{};
-    p.x = x;
-    p.x_type = in_type(x_dtype);
-    p.ldx = ldx;
-    p.gscale_in = g_used;
-    p.gscale_out = gscale_in ? gscale_out : nullptr;
-    p.a_codes_out = a_codes_out;
-    p.a_scales_out = a_scales_out;
-    p.g = g;
-    return hip_status(nvfp4::launch_linear_skinny(p, s), "nvfp4_w4a4_linear (fused skinny) launch");
-  }
-  hipError_t e = enqueue_quant_act(x, x_dtype, M, K, ldx, gscale_in, a_codes_out, a_scales_out, gscale_out, s);
-  if (e != hipSuccess) return hip_status(e, "nvfp4_w4a4_linear quantize launch");
-  g.a_codes = a_codes_out;
-  g.a_scales = a_scales_out;
-  g.a_gscale = gscale_out;
-  return hip_status(nvfp4::launch_gemm_tiled(g, s), "nvfp4_w4a4_linear gemm launch");
+  return linear_impl(x, x_dtype, M, K, ldx, gscale_in, gscale_out, g, nullptr, nullptr, ws,
+                     ws ? ws + noalloc_scales_offset(M, K) : nullptr, static_cast<hipStream_t>(stream));
 }
 
 int32_t nvfp4_requantize_weight(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, int32_t n_seg,

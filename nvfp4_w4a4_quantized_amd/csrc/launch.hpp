@@ -7,6 +7,11 @@
 namespace nvfp4 {
 
 constexpr int kMaxSeg = 64;
+constexpr int kMaxDevices = 64;
+// Size of the fixed workspace of nvfp4_w4a4_linear_noalloc: activation codes
+// (M * K / 2 bytes) at offset 0, scale bytes (M * K / 16) at the next 256-byte
+// boundary.
+constexpr int64_t kNoallocScratchBytes = int64_t(32) << 20;
 
 // Segment table passed to kernels by value.  end[i] = one past the last row
 // (output column) of segment i; scale[i] = host-given calibrated scale (static mode).
@@ -88,5 +93,9 @@ hipError_t launch_mx_quant(const void* x, InType t, int64_t M, int64_t K, int64_
 hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
                           const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y, bool bf16_out,
                           int64_t ldy, hipStream_t s);
+
+// noalloc.hip: this device's copy of the fixed workspace (kNoallocScratchBytes),
+// looked up once per device with that device current.
+hipError_t noalloc_scratch(void** ptr);
 
 }  // namespace nvfp4

@@ -115,6 +115,17 @@ def test_linear_validation(nv):
     assert st == nv.NVFP4_ERR_INVALID_ARG
 
 
+def test_linear_noalloc_validation(nv):
+    seg, n = _segs([256])
+
+    def call(M=4096, N=256, K=4096):
+        return nv.lib.nvfp4_w4a4_linear_noalloc(FAKE, 1, M, K, K, None, FAKE, N, FAKE, FAKE, n, seg, FAKE, None, FAKE,
+                                                1, N, None)
+    assert call(M=16384) == nv.NVFP4_ERR_INVALID_ARG and "workspace" in nv.nvfp4_last_error()
+    assert call(M=0) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(K=72) == nv.NVFP4_ERR_INVALID_ARG
+
+
 def test_binding_rejects_wrong_dtype(nv):
     import torch
     x = torch.zeros((4, 64), dtype=torch.float16)
