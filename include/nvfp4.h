@@ -248,6 +248,34 @@ NVFP4_API int32_t nvfp4_segment_mismatch_factor(int32_t n_seg, const float* seg_
 NVFP4_API int32_t nvfp4_require_single_scale(int32_t n_seg, const float* seg_gscale);
 
 /*
+ * Consumer of the GDN gate outputs: alpha = e^g and the gated delta rule ("Why
+ * Gated DeltaNet Survives 4-Bit Quantization" review page: background section,
+ * Eq. 2; mechanism step 2, Eq. 1; the spec list's state size K = V = 128).  Per
+ * value head h and token t = 0 .. T-1, with key/query head kh = h / (n_v_heads /
+ * n_k_heads) (consecutive value heads share a key head):
+ *   S_t = alpha_t S_{t-1} + beta_t k_t (v_t - S_{t-1}^T k_t)^T,  o_t = S_t^T q_t / sqrt(d_k)
+ * with alpha_t = e^{g_t}, in fp32.  The prediction that the write replaces is the
+ * state before the decay, as the equation is printed.
+ *   q, k      device fp32, [T][ldq], [T][ldk]: head kh at columns kh*d_k ..; 16-byte
+ *             aligned, ldq and ldk multiples of 4 (NVFP4_ERR_UNSUPPORTED otherwise)
+ *   v         device fp32, [T][ldv]: value head h at columns h*d_v ..
+ *   gates     device fp32, [T][ldg]: the gate epilogue's rows [g_0..g_{H-1} | beta_0..beta_{H-1}]
+ *             (H = n_v_heads, ldg >= 2 H), e.g. the output of nvfp4_w4a4_linear with a gate
+ *   state_in  device fp32 [n_v_heads][d_k][d_v] or NULL (zero initial state)
+ *   state_out device fp32 [n_v_heads][d_k][d_v] (output; may equal state_in)
+ *   o         device fp32 [T][ldo] (output): value head h at columns h*d_v ..; must not
+ *             overlap q, k, v or gates
+ * Supported: d_k == 128, d_v a multiple of 8.  The token chain is sequential; heads
+ * and state columns run in parallel.  Keys are expected normalized (unit L2 norm),
+ * which with beta in (0, 1) keeps every step a contraction; nothing here normalizes.
+ */
+NVFP4_API int32_t nvfp4_gdn_gated_delta(const float* q, int64_t ldq, const float* k, int64_t ldk,
+                              const float* v, int64_t ldv, const float* gates, int64_t ldg,
+                              int64_t T, int32_t n_k_heads, int32_t n_v_heads, int32_t d_k, int32_t d_v,
+                              const float* state_in, float* state_out, float* o, int64_t ldo,
+                              void* stream);
+
+/*
  * MXFP4 variant (the format the review page names as the next generalization,
  * future work / the paper's section 9): E2M1 codes packed as above, one E8M0 scale
  * byte b (value 2^(b-127)) per 32 elements, no global scale.  The format follows the

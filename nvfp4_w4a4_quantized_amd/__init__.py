@@ -29,7 +29,7 @@ NVFP4_MAX_SEGMENTS = 64
 
 EXPORTED = ["nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize_act", "nvfp4_pack_weight",
             "nvfp4_w4a4_gemm", "nvfp4_w4a4_linear", "nvfp4_w4a4_linear_noalloc", "nvfp4_requantize_weight", "nvfp4_segment_mismatch_factor",
-            "nvfp4_require_single_scale", "nvfp4_mxfp4_quantize", "nvfp4_mxfp4_gemm"]
+            "nvfp4_require_single_scale", "nvfp4_gdn_gated_delta", "nvfp4_mxfp4_quantize", "nvfp4_mxfp4_gemm"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -68,6 +68,8 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_segment_mismatch_factor.argtypes = [I32, P, ctypes.c_float, P, P]
     lib.nvfp4_require_single_scale.restype = I32
     lib.nvfp4_require_single_scale.argtypes = [I32, P]
+    lib.nvfp4_gdn_gated_delta.restype = I32
+    lib.nvfp4_gdn_gated_delta.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I32, I32, I32, I32, P, P, P, I64, P]
     lib.nvfp4_mxfp4_quantize.restype = I32
     lib.nvfp4_mxfp4_quantize.argtypes = [P, I32, I64, I64, I64, P, P, P]
     lib.nvfp4_mxfp4_gemm.restype = I32
@@ -235,6 +237,30 @@ def nvfp4_require_single_scale(seg_gscale: Sequence[float]) -> None:
     n = len(seg_gscale)
     arr = (ctypes.c_float * max(n, 1))(*[float(v) for v in seg_gscale])
     _check(lib.nvfp4_require_single_scale(n, arr))
+
+
+def nvfp4_gdn_gated_delta(q, k, v, gates, n_k_heads, n_v_heads, state_in, state_out, o, d_k=128,
+                          stream=None) -> None:
+    """The gated delta rule over T tokens: q, k [T, >= n_k_heads*d_k], v and o
+    [T, >= n_v_heads*d_v], gates [T, >= 2*n_v_heads] ([g | beta] rows), states
+    [n_v_heads, d_k, d_v] (state_in None = zeros); all fp32 on the device."""
+    torch = _torch()
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (gates, "gates"), (state_out, "state_out"), (o, "o")):
+        if t.dtype != torch.float32:
+            raise Nvfp4Error(NVFP4_ERR_UNSUPPORTED, f"{name} must be float32")
+    if state_in is not None and (state_in.dtype != torch.float32 or not state_in.is_contiguous()):
+        raise Nvfp4Error(NVFP4_ERR_UNSUPPORTED, "state_in must be contiguous float32")
+    if not state_out.is_contiguous():
+        raise Nvfp4Error(NVFP4_ERR_INVALID_ARG, "state_out must be contiguous")
+    T, _, ldq = _rows(q, "q")
+    _, _, ldk = _rows(k, "k")
+    _, _, ldv = _rows(v, "v")
+    _, _, ldg = _rows(gates, "gates")
+    _, _, ldo = _rows(o, "o")
+    d_v = state_out.shape[-1]
+    _check(lib.nvfp4_gdn_gated_delta(q.data_ptr(), ldq, k.data_ptr(), ldk, v.data_ptr(), ldv, gates.data_ptr(), ldg,
+                                     T, n_k_heads, n_v_heads, d_k, d_v, _ptr(state_in), state_out.data_ptr(),
+                                     o.data_ptr(), ldo, _stream(stream)))
 
 
 def empty_mx_packed(rows: int, K: int, device="cuda"):

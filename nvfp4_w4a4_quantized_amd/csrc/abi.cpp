@@ -439,6 +439,35 @@ int32_t nvfp4_require_single_scale(int32_t n_seg, const float* seg_gscale) {
   return ok();
 }
 
+int32_t nvfp4_gdn_gated_delta(const float* q, int64_t ldq, const float* k, int64_t ldk, const float* v, int64_t ldv,
+                              const float* gates, int64_t ldg, int64_t T, int32_t n_k_heads, int32_t n_v_heads,
+                              int32_t d_k, int32_t d_v, const float* state_in, float* state_out, float* o,
+                              int64_t ldo, void* stream) {
+  if (!q || !k || !v || !gates || !state_out || !o)
+    return fail(NVFP4_ERR_INVALID_ARG, "q, k, v, gates, state_out and o must not be NULL");
+  if (T <= 0 || n_k_heads <= 0 || n_v_heads <= 0 || d_k <= 0 || d_v <= 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "T, head counts and head dimensions must be positive");
+  if (n_v_heads % n_k_heads)
+    return fail(NVFP4_ERR_INVALID_ARG, "n_v_heads=%d is not a multiple of n_k_heads=%d", n_v_heads, n_k_heads);
+  if (!nvfp4::gdn_shape_ok(d_k, d_v))
+    return fail(NVFP4_ERR_UNSUPPORTED, "the recurrence supports d_k == 128 and d_v a multiple of 8 (d_k=%d d_v=%d)",
+                d_k, d_v);
+  if (ldq < (int64_t)n_k_heads * d_k || ldk < (int64_t)n_k_heads * d_k || ldv < (int64_t)n_v_heads * d_v ||
+      ldo < (int64_t)n_v_heads * d_v || ldg < 2 * (int64_t)n_v_heads)
+    return fail(NVFP4_ERR_INVALID_ARG, "a row stride is shorter than its row");
+  if (!aligned16(q) || !aligned16(k) || ldq % 4 || ldk % 4)
+    return fail(NVFP4_ERR_UNSUPPORTED, "q and k must be 16-byte aligned with 16-byte aligned rows");
+  if ((int64_t)n_v_heads * (d_v / 8) >= (int64_t(1) << 31)) return fail(NVFP4_ERR_UNSUPPORTED, "too many heads");
+  const int64_t lim = int64_t(1) << 31;
+  if (T * ldq * 4 >= lim || T * ldk * 4 >= lim || T * ldv * 4 >= lim || T * ldg * 4 >= lim || T * ldo >= lim)
+    return fail(NVFP4_ERR_UNSUPPORTED, "each of q, k, v, gates must span < 2^31 bytes");
+  int32_t st = check_device();
+  if (st) return st;
+  return hip_status(nvfp4::launch_gdn_delta(q, ldq, k, ldk, v, ldv, gates, ldg, T, n_k_heads, n_v_heads, d_v,
+                                            state_in, state_out, o, ldo, static_cast<hipStream_t>(stream)),
+                    "nvfp4_gdn_gated_delta launch");
+}
+
 int32_t nvfp4_mxfp4_quantize(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
                              uint8_t* scales, void* stream) {
   int32_t st = check_x(x, x_dtype, M, K, ldx, "x");

@@ -94,6 +94,14 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
                           const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y, bool bf16_out,
                           int64_t ldy, hipStream_t s);
 
+// gdn.hip: the gated delta-rule recurrence (d_k = 128, d_v % 8 == 0) over T tokens,
+// alpha = e^g and beta read from the gate rows [g | beta] (ldg >= 2 n_v_heads).
+bool gdn_shape_ok(int32_t d_k, int32_t d_v);
+hipError_t launch_gdn_delta(const float* q, int64_t ldq, const float* k, int64_t ldk, const float* v, int64_t ldv,
+                            const float* gates, int64_t ldg, int64_t T, int32_t n_k_heads, int32_t n_v_heads,
+                            int32_t d_v, const float* state_in, float* state_out, float* o, int64_t ldo,
+                            hipStream_t s);
+
 // noalloc.hip: this device's copy of the fixed workspace (kNoallocScratchBytes),
 // looked up once per device with that device current.
 hipError_t noalloc_scratch(void** ptr);

@@ -195,6 +195,26 @@ def test_single_scale_guard(nv):
     assert nv.lib.nvfp4_require_single_scale(2, None) == nv.NVFP4_ERR_INVALID_ARG
 
 
+def test_gdn_gated_delta_validation(nv):
+    def call(q=FAKE, k=FAKE, v=FAKE, g=FAKE, T=64, Hk=2, Hv=6, dk=128, dv=128, ldq=256, ldk=256, ldv=768, ldg=12,
+             ldo=768, s_out=FAKE, o=FAKE):
+        return nv.lib.nvfp4_gdn_gated_delta(q, ldq, k, ldk, v, ldv, g, ldg, T, Hk, Hv, dk, dv, None, s_out, o, ldo,
+                                            None)
+    assert call(q=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(o=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(s_out=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(T=0) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(Hv=5) == nv.NVFP4_ERR_INVALID_ARG and "multiple" in nv.nvfp4_last_error()
+    assert call(dk=64, ldq=128, ldk=128) == nv.NVFP4_ERR_UNSUPPORTED
+    assert call(dv=12, ldv=72, ldo=72) == nv.NVFP4_ERR_UNSUPPORTED
+    assert call(ldq=200) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(ldg=11) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(ldo=700) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(q=FAKE_ODD) == nv.NVFP4_ERR_UNSUPPORTED
+    assert call(ldk=258) == nv.NVFP4_ERR_UNSUPPORTED
+    assert call(T=1 << 20, ldv=768) == nv.NVFP4_ERR_UNSUPPORTED          # byte extents past 2^31
+
+
 def test_mxfp4_validation(nv):
     q = lambda K=64, ld=64, codes=FAKE: nv.lib.nvfp4_mxfp4_quantize(FAKE, 1, 4, K, ld, codes, FAKE, None)
     assert q(K=48, ld=48) == nv.NVFP4_ERR_INVALID_ARG and "multiple of 32" in nv.nvfp4_last_error()
