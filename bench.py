@@ -8,8 +8,11 @@ epilogue).  Also reported: the same with dynamic activation scaling (amax pass
 included), the decode GEMV (M=4, N=16384, K=5120) in GB/s of packed weight
 traffic with weight copies rotated past the 256 MB infinity cache, the GDN gates
 and MLP gate/up workloads, the shared-scale re-encoding of fused weights, the
-MXFP4 variant on the in_proj shape, and the CPU oracle's throughput on a bounded
-row sample of the headline workload.
+MXFP4 variant on the in_proj shape, the tiny linear's call latency, the GDN gate
+consumer (gated delta rule over 8192 tokens), the achievable HBM and MFMA rates
+measured by a plain copy and an MFMA-only kernel, and the CPU oracle's throughput on
+a bounded row sample of the headline workload.  Every timed workload reports the
+mean and the median, 10th and 90th percentiles of per-call HIP-event times.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--all]
 """
@@ -93,6 +96,39 @@ def timed_steps(step, steps):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def settle(step, seconds=0.4):
+    """Run `step` untimed for about `seconds`, before the warm-up steps, so that the
+    GPU has reached the clock it holds under this load when timing starts."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+
+
+def dist(ms_values):
+    """mean / median / p10 / p90 of per-call times (ms)."""
+    a = np.asarray(ms_values, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 5), "median": round(float(np.median(a)), 5),
+            "p10": round(float(np.percentile(a, 10)), 5), "p90": round(float(np.percentile(a, 90)), 5), "n": int(a.size)}
+
+
+def event_times(call, n):
+    """HIP-event duration (ms) of each of n calls, events on the launch stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        evs[i][0].record(stream)
+        call(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 def event_breakdown(step, steps):
     """Mean HIP-event durations (ms) of the two launches of a step, measured in a
     separate pass after the timed one (event records between launches would add
@@ -105,6 +141,8 @@ def event_breakdown(step, steps):
     torch.cuda.synchronize()
     first = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     second = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    event_breakdown.last = dict(total=[e[0].elapsed_time(e[2]) for e in evs], first=[e[0].elapsed_time(e[1]) for e in evs],
+                                second=[e[1].elapsed_time(e[2]) for e in evs])
     return first, second
 
 
@@ -130,10 +168,11 @@ def time_prefill(nv, xt, wc, ws, wg, seg_end, steps, warmup, static_g, y_dtype):
         if ev is not None:
             ev[2].record(stream)
 
+    settle(step)
     for _ in range(warmup):
         step()
     wall = timed_steps(step, steps)
-    q_ms, g_ms = event_breakdown(step, steps)
+    q_ms, g_ms = event_breakdown(step, max(steps, 50))
     return wall, q_ms, g_ms, y
 
 
@@ -166,21 +205,18 @@ def time_decode(nv, steps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     per_call = e0.elapsed_time(e1) / n
-    # single-call latency (an event pair around each call: includes launch overhead)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
-    for i in range(50):
+    # single-call times (an event pair around each call, rotated weights)
+    def one(i):
         c, s = copies[i % n_sets]
-        evs[i][0].record(stream)
         nv.nvfp4_w4a4_linear(xt, gstat, gout, c, s, wl.seg_end, wg, y, stream=stream)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    single = np.array([a.elapsed_time(b) for a, b in evs])
+    single = np.array(event_times(one, 240))
     w_bytes = wl.N * wl.K // 2 + wl.N * wl.K // 16
     alg_bytes = w_bytes + wl.M * wl.K * 2 + wl.M * wl.N * 2
     gbps = alg_bytes / (per_call * 1e-3) / 1e9
     return dict(workload=wl.name, us_per_call=round(per_call * 1e3, 3), gbps=round(gbps, 1),
                 frac_hbm=round(gbps / PEAK_HBM_GBPS, 4), algorithmic_bytes=alg_bytes,
                 single_call_us_median=round(float(np.median(single)) * 1e3, 3),
+                single_call_us={k: (round(v * 1e3, 3) if k != "n" else v) for k, v in dist(single).items()},
                 rotated_weight_sets=n_sets, calls=n, act_scale="static",
                 timing="back-to-back calls, rotated weight copies, one event pair around all calls")
 
@@ -215,12 +251,18 @@ def time_config(nv, name, steps, warmup):
     gout = torch.empty(1, dtype=torch.float32, device="cuda")
 
     fused = N <= 128 and K % 256 == 0          # the fused skinny-N linear: x read once
+    # HBM-bound (fused) workloads alternate between two copies of x so that the working
+    # set (2 x 335 MB) exceeds twice the 256 MB infinity cache
+    xs = [xt, xt.clone()] if fused else [xt]
+    turn = [0]
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         if fused:
-            nv.nvfp4_w4a4_linear(xt, gstat, gout, wc, ws, wl.seg_end, wg, y, gate=gate, stream=stream)
+            xi = xs[turn[0] % len(xs)]
+            turn[0] += 1
+            nv.nvfp4_w4a4_linear(xi, gstat, gout, wc, ws, wl.seg_end, wg, y, gate=gate, stream=stream)
             if ev is not None:
                 ev[1].record(stream)
         else:
@@ -231,10 +273,12 @@ def time_config(nv, name, steps, warmup):
         if ev is not None:
             ev[2].record(stream)
 
+    settle(step)
     for _ in range(warmup):
         step()
     wall = timed_steps(step, steps)
-    q_ms, g_ms = event_breakdown(step, steps)
+    q_ms, g_ms = event_breakdown(step, max(steps, 50))
+    step_dist = dist(event_breakdown.last["total"])
     flops = 2.0 * M * N * K
     ybytes = M * N * (2 if wl.y_dtype == "bf16" else 4)
     packed = lambda rows: rows * K // 2 + rows * K // 16
@@ -245,7 +289,8 @@ def time_config(nv, name, steps, warmup):
     breakdown = {"linear": round(q_ms, 4)} if fused else {"quantize_act": round(q_ms, 4), "gemm": round(g_ms, 4)}
     out = dict(workload=name, M=M, N=N, K=K, segments=wl.seg_end, mode=mode,
                ms_per_step=round(wall, 4), tflops=round(flops / (wall * 1e-3) / 1e12, 2),
-               breakdown_ms=breakdown,
+               breakdown_ms=breakdown, step_ms=step_dist,
+               input_sets=len(xs),
                algorithmic_bytes={"two_stage": two_stage_bytes, "fused_minimum": fused_bytes})
     if fused:
         gbps = fused_bytes / (wall * 1e-3) / 1e9
@@ -255,9 +300,101 @@ def time_config(nv, name, steps, warmup):
     else:
         out.update(bound="mfma", frac_mfma=round(flops / (wall * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
                    gemm_tflops=round(flops / (g_ms * 1e-3) / 1e12, 2))
-    del xt, wc, ws, ac, as_, y
+    del xt, xs, wc, ws, ac, as_, y
     torch.cuda.empty_cache()
     return out
+
+
+def time_tiny(nv, calls=200):
+    """The tiny linear (64 x 128 x 256, fp32 in and out, dynamic scales for both
+    operands): latency of one nvfp4_w4a4_linear call (amax pass + the fused skinny
+    kernel), HIP events around each call."""
+    import torch
+    from synth import workloads as W
+    wl = W.generate("tiny_linear_64x128x256")
+    xt = torch.from_numpy(wl.data["x32"]).cuda()
+    wt = torch.from_numpy(wl.data["w32"]).cuda()
+    wc, ws = nv.empty_packed(wl.N, wl.K, "cuda")
+    wg = torch.empty(1, dtype=torch.float32, device="cuda")
+    nv.nvfp4_pack_weight(wt, wl.seg_end, None, wc, ws, wg)
+    y = torch.empty((wl.M, wl.N), dtype=torch.float32, device="cuda")
+    g = torch.empty(1, dtype=torch.float32, device="cuda")
+    call = lambda i: nv.nvfp4_w4a4_linear(xt, None, g, wc, ws, wl.seg_end, wg, y)
+    for i in range(20):
+        call(i)
+    d = dist(event_times(call, calls))
+    return dict(workload=wl.name, mode="nvfp4_w4a4_linear, dynamic activation scale (amax pass + fused kernel)",
+                latency_us={k: (round(v * 1e3, 2) if k != "n" else v) for k, v in d.items()},
+                bound="launch latency")
+
+
+PEAK_FP32_VALU_TFLOPS = 157.3          # MI355X vector fp32 (packed); unpacked FMA: half of it
+
+
+def time_gdn(nv, steps, warmup):
+    """The GDN gate consumer: nvfp4_gdn_gated_delta over 8192 tokens with 16 key and
+    48 value heads, d_k = d_v = 128 (one sequence), inputs resident in HBM."""
+    import torch
+    from synth import workloads as W
+    T = 8192
+    hd = W.GDN_HEADS
+    inp = W.gdn_recurrence_inputs(T, **hd, seed=0)
+    q = torch.from_numpy(inp["q"].reshape(T, -1)).cuda()
+    k = torch.from_numpy(inp["k"].reshape(T, -1)).cuda()
+    v = torch.from_numpy(inp["v"].reshape(T, -1)).cuda()
+    gates = torch.from_numpy(inp["gates"]).cuda()
+    Hk, Hv, dk, dv = hd["n_k_heads"], hd["n_v_heads"], hd["d_k"], hd["d_v"]
+    o = torch.empty((T, Hv * dv), dtype=torch.float32, device="cuda")
+    st = torch.empty((Hv, dk, dv), dtype=torch.float32, device="cuda")
+    call = lambda i: nv.nvfp4_gdn_gated_delta(q, k, v, gates, Hk, Hv, None, st, o)
+    settle(lambda: call(0), 0.3)
+    for i in range(warmup):
+        call(i)
+    d = dist(event_times(call, max(steps, 20)))
+    flops = 7.0 * T * Hv * dk * dv          # S^T k, the decayed rank-one write, S^T q
+    bytes_ = 4 * T * (2 * Hk * dk + 2 * Hv * dv + 2 * Hv) + 4 * Hv * dk * dv
+    ms = d["median"]
+    return dict(workload="gdn_gated_delta_8192tok_16x48heads_128x128",
+                mode="alpha = e^g and the gated delta rule (Eq. 2), fp32, one sequence", ms=d,
+                tokens_per_s=round(T / (ms * 1e-3), 1), tflops=round(flops / (ms * 1e-3) / 1e12, 3),
+                bound="alu (sequential token chain)", peak_fp32_vector_tflops=PEAK_FP32_VALU_TFLOPS,
+                frac_fp32_vector=round(flops / (ms * 1e-3) / 1e12 / PEAK_FP32_VALU_TFLOPS, 4),
+                algorithmic_bytes=bytes_, gbps=round(bytes_ / (ms * 1e-3) / 1e9, 1),
+                us_per_token=round(ms * 1e3 / T, 4))
+
+
+def achievable_peaks(nv):
+    """Rates the chip sustains here, beside the datasheet peaks: a plain 1 GiB device
+    copy (bytes read + written per second) and a kernel that only issues f16 MFMAs."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    copy_ms = dist(event_times(lambda i: dst.copy_(src), 20))["median"]
+    del src, dst
+    blocks, iters = 256 * 4, 20000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    nv.nvfp4_bench_mfma_peak(2000, blocks, out)
+    mf_ms = dist(event_times(lambda i: nv.nvfp4_bench_mfma_peak(iters, blocks, out), 5))["median"]
+    mflops = blocks * 4 * iters * 4 * 32768.0
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbps": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
+            "hbm_copy_frac_of_datasheet": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "mfma_f16_tflops": round(mflops / (mf_ms * 1e-3) / 1e12, 1),
+            "mfma_f16_frac_of_datasheet": round(mflops / (mf_ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
+            "how": "torch copy of 1 GiB (2 GiB moved); MFMA 32x32x16 f16 only, 1024 workgroups x 4 waves"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 REQUANT_WORKLOADS = ["gdn_in_proj_8192x16384x5120", "mlp_gate_up_32768x34816x5120"]
@@ -368,7 +505,8 @@ def profile_target(nv, target, launches):
       decode - nvfp4_w4a4_linear, decode GEMV 4 x 16384 x 5120
       gates  - nvfp4_w4a4_linear, fused GDN gates 32768 x 96 x 5120
       requant - nvfp4_requantize_weight on the GDN in_proj weight (16384 x 5120)
-      mxgemm - nvfp4_mxfp4_gemm on the GDN in_proj shape (MXFP4 operands)"""
+      mxgemm - nvfp4_mxfp4_gemm on the GDN in_proj shape (MXFP4 operands)
+      gdn    - nvfp4_gdn_gated_delta, 8192 tokens, 16 key / 48 value heads"""
     import torch
     from synth import workloads as W
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
@@ -377,6 +515,19 @@ def profile_target(nv, target, launches):
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
+    if target == "gdn":
+        T = 8192
+        hd = W.GDN_HEADS
+        inp = W.gdn_recurrence_inputs(T, **hd, seed=0)
+        q, k, v = (torch.from_numpy(inp[n].reshape(T, -1)).cuda() for n in ("q", "k", "v"))
+        gates = torch.from_numpy(inp["gates"]).cuda()
+        o = torch.empty_like(v)
+        st = torch.empty((hd["n_v_heads"], hd["d_k"], hd["d_v"]), dtype=torch.float32, device="cuda")
+        for _ in range(launches):
+            nv.nvfp4_gdn_gated_delta(q, k, v, gates, hd["n_k_heads"], hd["n_v_heads"], None, st, o)
+        torch.cuda.synchronize()
+        print(f"profile target gdn: {launches} launches of the gated delta rule over {T} tokens", flush=True)
+        return
     name = {"gemm": "gdn_in_proj_8192x16384x5120", "quant": "gdn_in_proj_8192x16384x5120",
             "decode": "decode_gemv_4x16384x5120", "gates": "gdn_gates_32768x96x5120",
             "requant": "gdn_in_proj_8192x16384x5120", "mxgemm": "gdn_in_proj_8192x16384x5120"}[target]
@@ -441,6 +592,7 @@ def cpu_baseline(wl, static_g, target_s=10.0):
         used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     flops = 2.0 * rows * wl.N * wl.K
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(min(cores, used)), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{rows} of {wl.M} rows of the GDN in_proj workload (N={wl.N}, K={wl.K}): oracle "
                       f"quantize + float64 dequantize-GEMM + bf16 rounding, {t:.1f} s; oracle weight "
                       f"packing ({pack_s:.1f} s) untimed"}
@@ -457,7 +609,7 @@ def main():
     ap.add_argument("--decode-only", action="store_true", help="time only the decode GEMV (no JSON contract line)")
     ap.add_argument("--no-configs", action="store_true", help="skip the GDN-gates and MLP gate/up workloads")
     ap.add_argument("--configs-only", action="store_true", help="time only the GDN-gates and MLP gate/up workloads")
-    ap.add_argument("--profile-target", choices=["gemm", "quant", "decode", "gates", "requant", "mxgemm"],
+    ap.add_argument("--profile-target", choices=["gemm", "quant", "decode", "gates", "requant", "mxgemm", "gdn"],
                     help="for counter runs: a calibration copy, then a few launches of one kernel (no JSON line)")
     ap.add_argument("--launches", type=int, default=3)
     args = ap.parse_args()
@@ -520,6 +672,8 @@ def main():
                      "traffic": traffic_if_current(), "kernel": "k_gemm_big (256x256 tile, bf16 out)",
                      "kernel_ms": round(g_ms, 4)},
         "breakdown_ms": {"quantize_act": round(q_ms, 4), "gemm": round(g_ms, 4)},
+        "step_ms": dist(event_breakdown.last["total"]),
+        "gemm_ms": dist(event_breakdown.last["second"]),
     }
     if not args.no_dynamic:
         log("timing prefill (dynamic activation scale)")
@@ -543,6 +697,13 @@ def main():
         for n in REQUANT_WORKLOADS:
             log(f"timing the shared-scale re-encoding of the {n} weight")
             out["other_workloads"].append(time_requantize(nv, n, max(args.steps, 20), 5))
+    if not args.no_configs:
+        log("timing the tiny linear (64 x 128 x 256)")
+        out["tiny_linear"] = time_tiny(nv)
+        log("timing the GDN gate consumer (8192 tokens, 48 heads)")
+        out["gdn_recurrence"] = time_gdn(nv, args.steps, 3)
+        log("measuring achievable HBM and MFMA rates")
+        out["achievable_peaks"] = achievable_peaks(nv)
     if not args.no_cpu:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(wl, np.float32(gstat.item()))

@@ -302,6 +302,14 @@ NVFP4_API int32_t nvfp4_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scal
                          const uint8_t* w_codes, const uint8_t* w_scales, void* y, int32_t y_dtype, int64_t ldy,
                          void* stream);
 
+/*
+ * Measurement helper, not part of the layer: a kernel that only issues f16 MFMA
+ * 32x32x16 instructions (n_blocks workgroups of 4 waves, each wave 4 x iters of
+ * them, 32768 FLOP each), so that a benchmark can report the matrix rate the chip
+ * sustains beside its datasheet peak.  out: device, n_blocks * 256 fp32 (written).
+ */
+NVFP4_API int32_t nvfp4_bench_mfma_peak(int64_t iters, int32_t n_blocks, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

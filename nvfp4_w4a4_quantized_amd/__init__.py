@@ -29,7 +29,7 @@ NVFP4_MAX_SEGMENTS = 64
 
 EXPORTED = ["nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize_act", "nvfp4_pack_weight",
             "nvfp4_w4a4_gemm", "nvfp4_w4a4_linear", "nvfp4_w4a4_linear_noalloc", "nvfp4_requantize_weight", "nvfp4_segment_mismatch_factor",
-            "nvfp4_require_single_scale", "nvfp4_gdn_gated_delta", "nvfp4_mxfp4_quantize", "nvfp4_mxfp4_gemm"]
+            "nvfp4_require_single_scale", "nvfp4_gdn_gated_delta", "nvfp4_mxfp4_quantize", "nvfp4_mxfp4_gemm", "nvfp4_bench_mfma_peak"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -70,6 +70,8 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_require_single_scale.argtypes = [I32, P]
     lib.nvfp4_gdn_gated_delta.restype = I32
     lib.nvfp4_gdn_gated_delta.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I32, I32, I32, I32, P, P, P, I64, P]
+    lib.nvfp4_bench_mfma_peak.restype = I32
+    lib.nvfp4_bench_mfma_peak.argtypes = [I64, I32, P, P]
     lib.nvfp4_mxfp4_quantize.restype = I32
     lib.nvfp4_mxfp4_quantize.argtypes = [P, I32, I64, I64, I64, P, P, P]
     lib.nvfp4_mxfp4_gemm.restype = I32
@@ -285,3 +287,7 @@ def nvfp4_mxfp4_gemm(a_codes, a_scales, w_codes, w_scales, y, stream=None) -> No
     _check(lib.nvfp4_mxfp4_gemm(a_codes.data_ptr(), a_scales.data_ptr(), M, N, 2 * half_k, w_codes.data_ptr(),
                                 w_scales.data_ptr(), y.data_ptr(), _dtype_code(y), ldy, _stream(stream)))
 
+
+def nvfp4_bench_mfma_peak(iters: int, n_blocks: int, out, stream=None) -> None:
+    """Measurement helper: n_blocks x 4 waves issuing 4 * iters f16 MFMA 32x32x16 each."""
+    _check(lib.nvfp4_bench_mfma_peak(int(iters), int(n_blocks), out.data_ptr(), _stream(stream)))

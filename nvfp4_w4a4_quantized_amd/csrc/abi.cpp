@@ -468,6 +468,14 @@ int32_t nvfp4_gdn_gated_delta(const float* q, int64_t ldq, const float* k, int64
                     "nvfp4_gdn_gated_delta launch");
 }
 
+int32_t nvfp4_bench_mfma_peak(int64_t iters, int32_t n_blocks, float* out, void* stream) {
+  if (iters <= 0 || n_blocks <= 0 || !out) return fail(NVFP4_ERR_INVALID_ARG, "iters, n_blocks > 0 and out needed");
+  int32_t st = check_device();
+  if (st) return st;
+  return hip_status(nvfp4::launch_mfma_peak(iters, n_blocks, out, static_cast<hipStream_t>(stream)),
+                    "nvfp4_bench_mfma_peak launch");
+}
+
 int32_t nvfp4_mxfp4_quantize(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
                              uint8_t* scales, void* stream) {
   int32_t st = check_x(x, x_dtype, M, K, ldx, "x");

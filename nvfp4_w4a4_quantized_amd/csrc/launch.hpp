@@ -102,6 +102,10 @@ hipError_t launch_gdn_delta(const float* q, int64_t ldq, const float* k, int64_t
                             int32_t d_v, const float* state_in, float* state_out, float* o, int64_t ldo,
                             hipStream_t s);
 
+// probe.hip: n_blocks workgroups of 4 waves, each wave 4 x iters MFMA 32x32x16 f16;
+// out receives n_blocks * 256 floats.
+hipError_t launch_mfma_peak(int64_t iters, int32_t n_blocks, float* out, hipStream_t s);
+
 // noalloc.hip: this device's copy of the fixed workspace (kNoallocScratchBytes),
 // looked up once per device with that device current.
 hipError_t noalloc_scratch(void** ptr);

@@ -128,11 +128,14 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_linear_skinny(GemvArgs p) {
 #pragma unroll
   for (int i = 0; i < R - 1; ++i) xunit_load<T>(p.x, xoff + 128 * min<int64_t>(i, nu - 1), xr[i]);
 
-  // weight chunk 0 into buffer 0 (chunk c + 1 is loaded at the start of chunk c)
-  WStage<NT> ws;
-  wchunk_load<NT>(a, 0, ws);
-  wchunk_store<NT>(sk_lds, ws, a.N);
+  // Weight chunks: the raw chunk c + 2 is loaded at the start of chunk c (into stage
+  // c & 1) and decoded into LDS buffer (c + 1) & 1 during chunk c, so that the wait
+  // for its loads leaves the x loads of about four units in flight.
   const int64_t nc = K / SK_KC;
+  WStage<NT> ws[2];
+  wchunk_load<NT>(a, 0, ws[0]);
+  wchunk_load<NT>(a, min<int64_t>(1, nc - 1), ws[1]);
+  wchunk_store<NT>(sk_lds, ws[0], a.N);
 
   f32x4 acc[NT];
 #pragma unroll
@@ -154,25 +157,29 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_linear_skinny(GemvArgs p) {
   // B operand: weight row 16 j + rr, chunk column 128 (u % 2) + 32 q + 8 t
   const uint32_t bbase = (uint32_t)(rr * SK_ROWB + 64 * q);
 
-  for (int64_t u0 = 0; u0 < nu; u0 += R) {
+  // two chunks (four 128-element units) per iteration, so that every ring and stage
+  // index below is a compile-time constant (u0 % 4 == 0; nu is even)
+  for (int64_t u0 = 0; u0 < nu; u0 += 4) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < 4; ++r) {
       const int64_t u = u0 + r;
-      if (u >= nu) break;                                            // uniform
+      if (r == 2 && u >= nu) break;                                  // uniform
       const int64_t c = u >> 1;                                      // weight chunk
+      const int cp = r >> 1;                                         // c & 1
       if (r % 2 == 0) {
         // chunk boundary: chunk c was decoded into buffer c & 1 during chunk c - 1
         // (chunk 0: before the loop); the barrier publishes it and ends every wave's
-        // reads of buffer (c+1) & 1.  Stage chunk c + 1 (the last chunk again at the end).
-        __syncthreads();
-        wchunk_load<NT>(a, min<int64_t>(c + 1, nc - 1), ws);
+        // reads of buffer (c+1) & 1.  It waits for LDS traffic only: the x stream stays
+        // in flight across it.  Stage chunk c + 2 (the last chunk again at the end).
+        lds_sync();
+        wchunk_load<NT>(a, min<int64_t>(c + 2, nc - 1), ws[cp]);
       }
       // keep R - 1 units of x in flight (past the end: re-read the last unit)
       xunit_load<T>(p.x, xoff + 128 * min<int64_t>(u + R - 1, nu - 1), xr[(r + R - 1) % R]);
 
       // quantize the lane's two blocks (elements 32q .. 32q+31 of unit u)
       float v[32];
-      xunit_unpack<T>(xr[r], v);
+      xunit_unpack<T>(xr[r % R], v);
       uint32_t sb[2], w[4];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_linear_skinny(GemvArgs p) {
       }
       // MFMA 16x16x32 steps: A = the lane's elements 8t .. 8t+7, B = weight rows
       // 16 j + rr at the same K positions
-      const uint8_t* bl = sk_lds + (c & 1) * WBUF + bbase + 256 * (u & 1);
+      const uint8_t* bl = sk_lds + cp * WBUF + bbase + 256 * (r & 1);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         // all of this step's weight reads first, the decode of A under them
@@ -206,7 +213,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_linear_skinny(GemvArgs p) {
       }
       if (r % 2 == 1) {
         // decode the next weight chunk into the other buffer (free since the last barrier)
-        if (c + 1 < nc) wchunk_store<NT>(sk_lds + ((c + 1) & 1) * WBUF, ws, a.N);
+        if (c + 1 < nc) wchunk_store<NT>(sk_lds + (cp ^ 1) * WBUF, ws[cp ^ 1], a.N);
       }
     }
   }

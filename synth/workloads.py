@@ -178,3 +178,23 @@ def gdn_recurrence_inputs(T: int, n_k_heads: int = 16, n_v_heads: int = 48, d_k:
     if with_state:
         out["state0"] = (rng.standard_normal((n_v_heads, d_k, d_v)) * 0.1).astype(np.float32)
     return out
+
+
+# --------------------------------------------------------------------------- rotation parameters
+
+def krpbh_params(d: int, h: int = 512, seed: int = 0) -> dict:
+    """Random draws of a K-RPBH rotation of dimension d = k h: a uniform random
+    permutation perm (int32 [d]), Rademacher signs (int8 [d], +-1) and a Haar-random
+    orthogonal k x k matrix Q (fp32), drawn as the Q factor of a QR decomposition of
+    an N(0, 1) matrix with the signs of R's diagonal moved into Q (the standard way
+    to sample the Haar measure).  Draw order: perm, signs, the Gaussian matrix."""
+    if d % h:
+        raise ValueError("d must be a multiple of h")
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(d).astype(np.int32)
+    signs = np.where(rng.random(d) < 0.5, -1, 1).astype(np.int8)
+    k = d // h
+    A = rng.standard_normal((k, k))
+    q, r = np.linalg.qr(A)
+    q = q * np.sign(np.diag(r))[None, :]
+    return dict(perm=perm, signs=signs, Q=q.astype(np.float32), h=h)
