@@ -248,6 +248,59 @@ NVFP4_API int32_t nvfp4_segment_mismatch_factor(int32_t n_seg, const float* seg_
 NVFP4_API int32_t nvfp4_require_single_scale(int32_t n_seg, const float* seg_gscale);
 
 /*
+ * Rotated NVFP4 front end (SoloQ-N; "SoloQ: Calibration-Free Quantization for
+ * Diffusion Language Models" page, "how it is used" and "assumptions and limits"
+ * sections): every row x of the input is rotated, z = Pi x with the K-RPBH rotation
+ * Pi = (Q_k (x) I_h) blkdiag(H_h D_1, ..., H_h D_k) P, quantized to NVFP4 by the
+ * numerics above with global scales computed from the rotated rows, and given the
+ * scale-only bias correction c_bc(z) = ||z||^2 / <q(z), z> (q(z) the dequantized
+ * NVFP4 row; 1 when that product is 0).  Activations are rotated online (one
+ * segment); a weight W is rotated offline the same way, row by row (its rows become
+ * those of W' = W Pi^T), with one global scale per segment.
+ *   x, x_dtype, rows, K, ldx   as for nvfp4_quantize_act / nvfp4_pack_weight
+ *   h          block size: 512; K = k * h with k in {1, 2, 4, 8, 10}
+ *              (NVFP4_ERR_UNSUPPORTED otherwise)
+ *   perm       device int32 [K]: a permutation of 0..K-1, (P x)_i = x[perm[i]]
+ *              (entries outside 0..K-1 are clamped; the result is then meaningless)
+ *   signs      device int8 [K]: +1 or -1 (negative = -1), the diagonal of D_1..D_k in
+ *              the permuted order
+ *   Q          device fp32 [k][k] row-major: the cross-block mixer, block r of z is
+ *              sum_s Q[r][s] (H_h D_s P x)_s
+ *   n_seg, seg_end, seg_gscale_in  as for nvfp4_pack_weight (NULL scales = dynamic:
+ *              fp32(amax / 2688) of each segment's rotated rows; activations: one segment)
+ *   codes, scales   device outputs [rows][K/2], [rows][K/16]
+ *   seg_gscale_out  device, n_seg fp32 (output)
+ *   cbc_out    device, rows fp32 (output): c_bc of every row
+ *   z_out      device fp32 [rows][K] or NULL: the rotated rows (16-byte aligned)
+ * The rotation is evaluated in fp32 in one fixed order (gather and sign, the
+ * Walsh-Hadamard butterflies at pair distance 1, 2, ..., h/2 with lower a + b and
+ * upper a - b, one multiply by fp32(1/sqrt(h)), then left-to-right sums of
+ * separately rounded products Q[r][s] y_s), so that the codes are reproducible.
+ * In dynamic mode the rows are rotated twice (once for the global scale).
+ */
+NVFP4_API int32_t nvfp4_rotate_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t K, int64_t ldx,
+                              int32_t h, const int32_t* perm, const int8_t* signs, const float* Q,
+                              int32_t n_seg, const int64_t* seg_end, const float* seg_gscale_in,
+                              uint8_t* codes, uint8_t* scales, float* seg_gscale_out, float* cbc_out,
+                              float* z_out, void* stream);
+
+/*
+ * The GEMM of nvfp4_w4a4_gemm with the bias corrections of the rotated front end
+ * folded into its epilogue (SoloQ page, "assumptions and limits": c_bc is absorbed by
+ * the per-token and per-row scales): y[m,n] = fp32(fp32(acc * fp32(alpha_n *
+ * col_scale[n])) * row_scale[m]) with alpha_n = g_a * g_w[segment(n)], rounded once
+ * to y_dtype.  row_scale: device fp32 [M] (the activations' c_bc), col_scale: device
+ * fp32 [N] (the weight rows' c_bc); both required.  No gate epilogue.  Other
+ * arguments as for nvfp4_w4a4_gemm.
+ */
+NVFP4_API int32_t nvfp4_w4a4_gemm_rowcol(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                               int64_t M, int64_t N, int64_t K,
+                               const uint8_t* w_codes, const uint8_t* w_scales,
+                               int32_t n_seg, const int64_t* seg_end, const float* w_seg_gscale,
+                               const float* row_scale, const float* col_scale,
+                               void* y, int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
  * Consumer of the GDN gate outputs: alpha = e^g and the gated delta rule ("Why
  * Gated DeltaNet Survives 4-Bit Quantization" review page: background section,
  * Eq. 2; mechanism step 2, Eq. 1; the spec list's state size K = V = 128).  Per

@@ -29,7 +29,8 @@ NVFP4_MAX_SEGMENTS = 64
 
 EXPORTED = ["nvfp4_abi_version", "nvfp4_last_error", "nvfp4_quantize_act", "nvfp4_pack_weight",
             "nvfp4_w4a4_gemm", "nvfp4_w4a4_linear", "nvfp4_w4a4_linear_noalloc", "nvfp4_requantize_weight", "nvfp4_segment_mismatch_factor",
-            "nvfp4_require_single_scale", "nvfp4_gdn_gated_delta", "nvfp4_mxfp4_quantize", "nvfp4_mxfp4_gemm", "nvfp4_bench_mfma_peak"]
+            "nvfp4_require_single_scale", "nvfp4_rotate_quantize", "nvfp4_w4a4_gemm_rowcol",
+            "nvfp4_gdn_gated_delta", "nvfp4_mxfp4_quantize", "nvfp4_mxfp4_gemm", "nvfp4_bench_mfma_peak"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -68,6 +69,10 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_segment_mismatch_factor.argtypes = [I32, P, ctypes.c_float, P, P]
     lib.nvfp4_require_single_scale.restype = I32
     lib.nvfp4_require_single_scale.argtypes = [I32, P]
+    lib.nvfp4_rotate_quantize.restype = I32
+    lib.nvfp4_rotate_quantize.argtypes = [P, I32, I64, I64, I64, I32, P, P, P, I32, P, P, P, P, P, P, P, P]
+    lib.nvfp4_w4a4_gemm_rowcol.restype = I32
+    lib.nvfp4_w4a4_gemm_rowcol.argtypes = [P, P, P, I64, I64, I64, P, P, I32, P, P, P, P, P, I32, I64, P]
     lib.nvfp4_gdn_gated_delta.restype = I32
     lib.nvfp4_gdn_gated_delta.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I32, I32, I32, I32, P, P, P, I64, P]
     lib.nvfp4_bench_mfma_peak.restype = I32
@@ -239,6 +244,34 @@ def nvfp4_require_single_scale(seg_gscale: Sequence[float]) -> None:
     n = len(seg_gscale)
     arr = (ctypes.c_float * max(n, 1))(*[float(v) for v in seg_gscale])
     _check(lib.nvfp4_require_single_scale(n, arr))
+
+
+def nvfp4_rotate_quantize(x, perm, signs, Q, codes, scales, seg_gscale_out, cbc_out, seg_end=None,
+                          seg_gscale_in=None, z_out=None, h=512, stream=None) -> None:
+    """Rotate the rows of x (K-RPBH: perm int32 [K], signs int8 [K], Q fp32 [k, k], all
+    on the device), quantize them to NVFP4 with scales from the rotated rows (or the
+    host seg_gscale_in), and write the bias-correction factor of every row."""
+    rows, K, ldx = _rows(x, "x")
+    seg, n_seg = _seg_array([rows] if seg_end is None else seg_end)
+    gin = None
+    if seg_gscale_in is not None:
+        gin = (ctypes.c_float * n_seg)(*[float(v) for v in seg_gscale_in])
+    _check(lib.nvfp4_rotate_quantize(x.data_ptr(), _dtype_code(x), rows, K, ldx, h, perm.data_ptr(), signs.data_ptr(),
+                                     Q.data_ptr(), n_seg, seg, gin, codes.data_ptr(), scales.data_ptr(),
+                                     seg_gscale_out.data_ptr(), cbc_out.data_ptr(), _ptr(z_out), _stream(stream)))
+
+
+def nvfp4_w4a4_gemm_rowcol(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_end, w_seg_gscale, row_scale,
+                           col_scale, y, stream=None) -> None:
+    """The block-scaled GEMM with per-row and per-column output factors."""
+    M, half_k = a_codes.shape
+    N = w_codes.shape[0]
+    _, _, ldy = _rows(y, "y")
+    seg, n_seg = _seg_array(seg_end)
+    _check(lib.nvfp4_w4a4_gemm_rowcol(a_codes.data_ptr(), a_scales.data_ptr(), a_gscale.data_ptr(), M, N, 2 * half_k,
+                                      w_codes.data_ptr(), w_scales.data_ptr(), n_seg, seg, w_seg_gscale.data_ptr(),
+                                      row_scale.data_ptr(), col_scale.data_ptr(), y.data_ptr(), _dtype_code(y), ldy,
+                                      _stream(stream)))
 
 
 def nvfp4_gdn_gated_delta(q, k, v, gates, n_k_heads, n_v_heads, state_in, state_out, o, d_k=128,

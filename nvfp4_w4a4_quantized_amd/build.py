@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["abi.cpp", "quant.hip", "gemm.hip", "gemv.hip", "skinny.hip", "requant.hip", "mx.hip", "noalloc.hip", "gdn.hip", "probe.hip"]
+SOURCES = ["abi.cpp", "quant.hip", "gemm.hip", "gemv.hip", "skinny.hip", "requant.hip", "mx.hip", "noalloc.hip", "gdn.hip", "probe.hip", "soloq.hip"]
 
 COMPILE_FLAGS = [
     "--offload-arch=gfx950",

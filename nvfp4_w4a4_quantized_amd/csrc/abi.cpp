@@ -468,6 +468,53 @@ int32_t nvfp4_gdn_gated_delta(const float* q, int64_t ldq, const float* k, int64
                     "nvfp4_gdn_gated_delta launch");
 }
 
+int32_t nvfp4_rotate_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t K, int64_t ldx, int32_t h,
+                              const int32_t* perm, const int8_t* signs, const float* Q, int32_t n_seg,
+                              const int64_t* seg_end, const float* seg_gscale_in, uint8_t* codes, uint8_t* scales,
+                              float* seg_gscale_out, float* cbc_out, float* z_out, void* stream) {
+  int32_t st = check_x(x, x_dtype, rows, K, ldx, "x");
+  if (st) return st;
+  st = check_packed(codes, scales, "output");
+  if (st) return st;
+  if (!perm || !signs || !Q) return fail(NVFP4_ERR_INVALID_ARG, "perm, signs and Q must not be NULL");
+  if (!seg_gscale_out || !cbc_out) return fail(NVFP4_ERR_INVALID_ARG, "seg_gscale_out and cbc_out must not be NULL");
+  if (!nvfp4::rotate_shape_ok(K, h))
+    return fail(NVFP4_ERR_UNSUPPORTED, "the rotation supports h = 512 and K = k * 512 with k in {1, 2, 4, 8, 10} "
+                "(K=%lld h=%d)", (long long)K, h);
+  if (z_out && (reinterpret_cast<uintptr_t>(z_out) & 15u))
+    return fail(NVFP4_ERR_UNSUPPORTED, "z_out must be 16-byte aligned");
+  nvfp4::SegTable seg;
+  st = build_seg(n_seg, seg_end, rows, seg_gscale_in, &seg);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  return hip_status(nvfp4::launch_rotate_quant(x, in_type(x_dtype), rows, K, ldx, perm, signs, Q, seg,
+                                               seg_gscale_in == nullptr, codes, scales, seg_gscale_out, cbc_out,
+                                               z_out, static_cast<hipStream_t>(stream)),
+                    "nvfp4_rotate_quantize launch");
+}
+
+int32_t nvfp4_w4a4_gemm_rowcol(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale, int64_t M,
+                               int64_t N, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales, int32_t n_seg,
+                               const int64_t* seg_end, const float* w_seg_gscale, const float* row_scale,
+                               const float* col_scale, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  nvfp4::GemmArgs g{};
+  int32_t st = check_packed(a_codes, a_scales, "activation");
+  if (st) return st;
+  if (!a_gscale) return fail(NVFP4_ERR_INVALID_ARG, "a_gscale is NULL");
+  if (!row_scale || !col_scale) return fail(NVFP4_ERR_INVALID_ARG, "row_scale and col_scale must not be NULL");
+  st = check_gemm_common(M, N, K, w_codes, w_scales, n_seg, seg_end, w_seg_gscale, nullptr, y, y_dtype, ldy, &g);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  g.a_codes = a_codes;
+  g.a_scales = a_scales;
+  g.a_gscale = a_gscale;
+  g.row_scale = row_scale;
+  g.col_scale = col_scale;
+  return hip_status(nvfp4::launch_gemm_tiled(g, static_cast<hipStream_t>(stream)), "nvfp4_w4a4_gemm_rowcol launch");
+}
+
 int32_t nvfp4_bench_mfma_peak(int64_t iters, int32_t n_blocks, float* out, void* stream) {
   if (iters <= 0 || n_blocks <= 0 || !out) return fail(NVFP4_ERR_INVALID_ARG, "iters, n_blocks > 0 and out needed");
   int32_t st = check_device();

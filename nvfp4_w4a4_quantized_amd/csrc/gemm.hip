@@ -71,7 +71,7 @@ __device__ __forceinline__ uint32_t load_scales4(const uint8_t* base, int64_t ro
   }
 }
 
-template <bool ALIGNED, int EPI>
+template <bool ALIGNED, int EPI, bool RC>
 __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
   __shared__ u32x4 lds_ca[2][TBM];
   __shared__ u32x4 lds_cw[2][TBN];
@@ -165,13 +165,18 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
   for (int j = 0; j < 2; ++j) {
     const int64_t n = n0 + wn * 64 + j * 32 + li;
     const bool n_ok = n < a.N;
-    const float alpha = n_ok ? col_alpha<EPI>(a, n, ga) : 0.0f;
+    float alpha = n_ok ? col_alpha<EPI>(a, n, ga) : 0.0f;
+    if constexpr (RC) alpha = n_ok ? alpha * a.col_scale[n] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (n_ok && m < a.M) store_out<EPI>(a, m, n, acc[i][j][r], alpha);
+        if constexpr (RC) {
+          if (n_ok && m < a.M) store_out_rc<EPI>(a, m, n, acc[i][j][r], alpha, a.row_scale[m]);
+        } else {
+          if (n_ok && m < a.M) store_out<EPI>(a, m, n, acc[i][j][r], alpha);
+        }
       }
   }
 }
@@ -225,7 +230,7 @@ __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, uint8
 constexpr int GST = 4;                                  // LDS stages
 constexpr int ST_A = 0, ST_W = 8192, ST_SA = 16384, ST_SW = 17408, ST_BYTES = 18432;
 
-template <int EPI>
+template <int EPI, bool RC>
 __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[GST * ST_BYTES];
 
@@ -417,10 +422,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   for (int j = 0; j < 4; ++j) {
     const int64_t n = n0 + wn * 128 + j * 32 + li;
     alpha[j] = col_alpha<EPI>(a, min<int64_t>(n, a.N - 1), ga);
+    if constexpr (RC) alpha[j] = alpha[j] * a.col_scale[min<int64_t>(n, a.N - 1)];
   }
   static_assert(EPI != EPI_GATE, "the gate epilogue runs in the 128x128-tile kernel");
   constexpr int ESZ = (EPI == EPI_BF16) ? 2 : 4;
   const int64_t extent = ((a.M - 1) * a.ldy + a.N) * ESZ;
+  // per-row factors of this lane's 64 rows (rows past M read row M - 1, never stored)
+  float rsc[4][16];
+  if constexpr (RC) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        rsc[i][r] = a.row_scale[min<int64_t>(m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3), a.M - 1)];
+  }
+  auto scaled = [&](int i, int j, int r) {
+    const float v = acc[i][j][r] * alpha[j];
+    if constexpr (RC) return v * rsc[i][r];
+    else return v;
+  };
   if (m0 + GBM <= a.M && n0 + GBN <= a.N && extent < (int64_t(1) << 32) && (a.ldy % 2) == 0) {
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, (int)(uint32_t)extent, 0x00020000);
     const uint32_t ldyb = (uint32_t)a.ldy * ESZ;
@@ -438,7 +458,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
           for (int p = 0; p < 8; ++p) {
             typedef float f32x2 __attribute__((ext_vector_type(2)));
             typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            const f32x2 v = {acc[i][j][2 * p] * alpha[j], acc[i][j][2 * p + 1] * alpha[j]};
+            const f32x2 v = {scaled(i, j, 2 * p), scaled(i, j, 2 * p + 1)};
             const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
             const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp((int)pk, (int)pk, 0xB1, 0xF, 0xF, false);
             const uint32_t word = __builtin_amdgcn_perm(nb, pk, sel);
@@ -454,7 +474,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldyb + (uint32_t)(j * 128);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r] * alpha[j]), yr, voff, soff, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(scaled(i, j, r)), yr, voff, soff, 0);
           }
     }
     return;
@@ -468,7 +488,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (n_ok && m < a.M) store_out<EPI>(a, m, n, acc[i][j][r], alpha[j]);
+        if constexpr (RC) {
+          if (n_ok && m < a.M) store_out_rc<EPI>(a, m, n, acc[i][j][r], alpha[j], rsc[i][r]);
+        } else {
+          if (n_ok && m < a.M) store_out<EPI>(a, m, n, acc[i][j][r], alpha[j]);
+        }
       }
   }
 }
@@ -476,29 +500,34 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
 
 }  // namespace
 
-template <int EPI>
+template <int EPI, bool RC>
 static hipError_t launch_gemm_epi(const GemmArgs& a, hipStream_t s) {
   // k_gemm_big addresses each packed operand with 32-bit offsets
   const bool offsets32 = a.M * (a.K / 2) < (int64_t(1) << 31) && a.N * (a.K / 2) < (int64_t(1) << 31);
   if (EPI != EPI_GATE && a.K % GBK == 0 && a.K >= 3 * GBK && a.M >= 512 && a.N >= 512 && offsets32) {
     const int64_t big_tiles = ((a.M + GBM - 1) / GBM) * ((a.N + GBN - 1) / GBN);
     if constexpr (EPI != EPI_GATE) {
-      hipLaunchKernelGGL(k_gemm_big<EPI>, dim3((unsigned)big_tiles), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((k_gemm_big<EPI, RC>), dim3((unsigned)big_tiles), dim3(256), 0, s, a);
       return hipGetLastError();
     }
   }
   const int64_t tiles = ((a.M + TBM - 1) / TBM) * ((a.N + TBN - 1) / TBN);
   if (a.K % 64 == 0)
-    hipLaunchKernelGGL((k_gemm_tiled<true, EPI>), dim3((unsigned)tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm_tiled<true, EPI, RC>), dim3((unsigned)tiles), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemm_tiled<false, EPI>), dim3((unsigned)tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm_tiled<false, EPI, RC>), dim3((unsigned)tiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) {
-  if (a.gate.n_heads > 0) return launch_gemm_epi<EPI_GATE>(a, s);
-  if (a.y_type == OutType::BF16) return launch_gemm_epi<EPI_BF16>(a, s);
-  return launch_gemm_epi<EPI_F32>(a, s);
+  if (a.row_scale != nullptr || a.col_scale != nullptr) {
+    if (a.row_scale == nullptr || a.col_scale == nullptr || a.gate.n_heads > 0) return hipErrorInvalidValue;
+    if (a.y_type == OutType::BF16) return launch_gemm_epi<EPI_BF16, true>(a, s);
+    return launch_gemm_epi<EPI_F32, true>(a, s);
+  }
+  if (a.gate.n_heads > 0) return launch_gemm_epi<EPI_GATE, false>(a, s);
+  if (a.y_type == OutType::BF16) return launch_gemm_epi<EPI_BF16, false>(a, s);
+  return launch_gemm_epi<EPI_F32, false>(a, s);
 }
 
 }  // namespace nvfp4

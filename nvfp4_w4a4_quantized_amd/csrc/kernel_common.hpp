@@ -63,6 +63,19 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int64_t m, int64_t 
   }
 }
 
+// Epilogue with per-row and per-column factors: y = (acc * fp32(alpha * col)) * row,
+// every product rounded once (alpha * col is folded into the caller's alpha).
+template <int EPI>
+__device__ __forceinline__ void store_out_rc(const GemmArgs& a, int64_t m, int64_t n, float acc, float alpha_col,
+                                             float row) {
+  static_assert(EPI != EPI_GATE, "no gate epilogue with row/column factors");
+  const float v = (acc * alpha_col) * row;
+  if constexpr (EPI == EPI_BF16) {
+    reinterpret_cast<uint16_t*>(a.y)[m * a.ldy + n] = (uint16_t)f32_to_bf16_bits(v);
+  } else {
+    reinterpret_cast<float*>(a.y)[m * a.ldy + n] = v;
+  }
+}
 
 __device__ __forceinline__ float dpp_swap_adjacent(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));

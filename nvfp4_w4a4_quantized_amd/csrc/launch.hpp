@@ -55,6 +55,10 @@ struct GemmArgs {
   void* y;
   OutType y_type;
   int64_t ldy;
+  // optional per-row (m) and per-column (n) fp32 output factors (the rotated front
+  // end's bias corrections); NULL = none.  Supported by launch_gemm_tiled only.
+  const float* row_scale;
+  const float* col_scale;
 };
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s);
 
@@ -105,6 +109,16 @@ hipError_t launch_gdn_delta(const float* q, int64_t ldq, const float* k, int64_t
 // probe.hip: n_blocks workgroups of 4 waves, each wave 4 x iters MFMA 32x32x16 f16;
 // out receives n_blocks * 256 floats.
 hipError_t launch_mfma_peak(int64_t iters, int32_t n_blocks, float* out, hipStream_t s);
+
+// soloq.hip: rotate rows (K = k * 512, k in {1, 2, 4, 8, 10}), quantize them to
+// NVFP4 with per-segment global scales (dynamic: from the rotated rows; else the host
+// values in seg.scale), write the bias-correction factor of every row and, when
+// z_out is not NULL, the rotated rows in fp32.
+bool rotate_shape_ok(int64_t K, int32_t h);
+hipError_t launch_rotate_quant(const void* x, InType t, int64_t rows, int64_t K, int64_t ldx, const int32_t* perm,
+                               const int8_t* signs, const float* Q, const SegTable& seg, bool dynamic,
+                               uint8_t* codes, uint8_t* scales, float* seg_gscale_out, float* cbc, float* z_out,
+                               hipStream_t s);
 
 // noalloc.hip: this device's copy of the fixed workspace (kNoallocScratchBytes),
 // looked up once per device with that device current.

@@ -195,6 +195,36 @@ def test_single_scale_guard(nv):
     assert nv.lib.nvfp4_require_single_scale(2, None) == nv.NVFP4_ERR_INVALID_ARG
 
 
+def test_rotate_quantize_validation(nv):
+    seg, n = _segs([64])
+
+    def call(x=FAKE, rows=64, K=1024, ld=1024, h=512, perm=FAKE, codes=FAKE, cbc=FAKE, z=None, segs=(seg, n)):
+        return nv.lib.nvfp4_rotate_quantize(x, 1, rows, K, ld, h, perm, FAKE, FAKE, segs[1], segs[0], None, codes,
+                                            FAKE, FAKE, cbc, z, None)
+    assert call(K=1536, ld=1536) == nv.NVFP4_ERR_UNSUPPORTED and "512" in nv.nvfp4_last_error()   # k = 3
+    assert call(h=256) == nv.NVFP4_ERR_UNSUPPORTED
+    assert call(K=8192, ld=8192) == nv.NVFP4_ERR_UNSUPPORTED                                       # k = 16
+    assert call(perm=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(cbc=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(codes=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(x=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(rows=0) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(z=FAKE_ODD) == nv.NVFP4_ERR_UNSUPPORTED
+    assert call(segs=_segs([32, 60])) == nv.NVFP4_ERR_INVALID_ARG        # segments must end at rows
+
+
+def test_gemm_rowcol_validation(nv):
+    seg, n = _segs([128])
+
+    def call(rs=FAKE, cs=FAKE, M=64, N=128, K=256):
+        return nv.lib.nvfp4_w4a4_gemm_rowcol(FAKE, FAKE, FAKE, M, N, K, FAKE, FAKE, n, seg, FAKE, rs, cs, FAKE, 1, N,
+                                             None)
+    assert call(rs=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(cs=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(K=40) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(N=100) == nv.NVFP4_ERR_INVALID_ARG                        # segment table != N
+
+
 def test_gdn_gated_delta_validation(nv):
     def call(q=FAKE, k=FAKE, v=FAKE, g=FAKE, T=64, Hk=2, Hv=6, dk=128, dv=128, ldq=256, ldk=256, ldv=768, ldg=12,
              ldo=768, s_out=FAKE, o=FAKE):
