@@ -363,6 +363,60 @@ def time_gdn(nv, steps, warmup):
                 us_per_token=round(ms * 1e3 / T, 4))
 
 
+def time_rotated(nv, steps, warmup):
+    """The rotated NVFP4 front end on the GDN in_proj shape (8192 x 16384 x 5120, 4
+    weight segments): the weight is rotated and packed once (offline); one step =
+    nvfp4_rotate_quantize of the activations (dynamic: a rotate+amax pass, then rotate,
+    quantize and c_bc) + nvfp4_w4a4_gemm_rowcol (the GEMM with the c_bc factors)."""
+    import torch
+    from synth import workloads as W
+    wl = W.generate("gdn_in_proj_8192x16384x5120")
+    M, N, K = wl.M, wl.N, wl.K
+    p = W.krpbh_params(K, 512, seed=0)
+    perm, signs, Q = (torch.from_numpy(p[n]).cuda() for n in ("perm", "signs", "Q"))
+    xt = dev_bf16(wl.data["x_bf16"])
+    wt = torch.from_numpy(wl.data["w32"]).cuda()
+    wl.data.clear()
+    wc, ws = nv.empty_packed(N, K, "cuda")
+    wg = torch.empty(len(wl.seg_end), dtype=torch.float32, device="cuda")
+    cw = torch.empty(N, dtype=torch.float32, device="cuda")
+    nv.nvfp4_rotate_quantize(wt, perm, signs, Q, wc, ws, wg, cw, seg_end=wl.seg_end)
+    torch.cuda.synchronize()
+    del wt
+    ac, as_ = nv.empty_packed(M, K, "cuda")
+    ag = torch.empty(1, dtype=torch.float32, device="cuda")
+    cx = torch.empty(M, dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        nv.nvfp4_rotate_quantize(xt, perm, signs, Q, ac, as_, ag, cx, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        nv.nvfp4_w4a4_gemm_rowcol(ac, as_, ag, wc, ws, wl.seg_end, wg, cx, cw, y, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    settle(step)
+    for _ in range(warmup):
+        step()
+    wall = timed_steps(step, steps)
+    r_ms, g_ms = event_breakdown(step, max(steps, 20))
+    flops = 2.0 * M * N * K
+    rot_bytes = 2 * (M * K * 2) + M * K // 2 + M * K // 16 + 4 * M     # x read twice, codes, scales, c_bc
+    del xt, wc, ws, ac, as_, y
+    torch.cuda.empty_cache()
+    return dict(workload="rotated_gdn_in_proj_8192x16384x5120",
+                mode="K-RPBH rotation (h = 512, k = 10) + NVFP4 (dynamic) + c_bc, then the GEMM with c_bc factors",
+                ms_per_step=round(wall, 4), tflops=round(flops / (wall * 1e-3) / 1e12, 2),
+                breakdown_ms={"rotate_quantize": round(r_ms, 4), "gemm_rowcol": round(g_ms, 4)},
+                step_ms=dist(event_breakdown.last["total"]),
+                gemm_tflops=round(flops / (g_ms * 1e-3) / 1e12, 2),
+                rotate_gbps=round(rot_bytes / (r_ms * 1e-3) / 1e9, 1), rotate_algorithmic_bytes=rot_bytes)
+
+
 def achievable_peaks(nv):
     """Rates the chip sustains here, beside the datasheet peaks: a plain 1 GiB device
     copy (bytes read + written per second) and a kernel that only issues f16 MFMAs."""
@@ -700,6 +754,8 @@ def main():
     if not args.no_configs:
         log("timing the tiny linear (64 x 128 x 256)")
         out["tiny_linear"] = time_tiny(nv)
+        log("timing the rotated front end on the GDN in_proj shape")
+        out["other_workloads"].append(time_rotated(nv, args.steps, args.warmup))
         log("timing the GDN gate consumer (8192 tokens, 48 heads)")
         out["gdn_recurrence"] = time_gdn(nv, args.steps, 3)
         log("measuring achievable HBM and MFMA rates")
