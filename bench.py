@@ -560,7 +560,8 @@ def profile_target(nv, target, launches):
       gates  - nvfp4_w4a4_linear, fused GDN gates 32768 x 96 x 5120
       requant - nvfp4_requantize_weight on the GDN in_proj weight (16384 x 5120)
       mxgemm - nvfp4_mxfp4_gemm on the GDN in_proj shape (MXFP4 operands)
-      gdn    - nvfp4_gdn_gated_delta, 8192 tokens, 16 key / 48 value heads"""
+      gdn    - nvfp4_gdn_gated_delta, 8192 tokens, 16 key / 48 value heads
+      rotate - nvfp4_rotate_quantize (dynamic) on the GDN in_proj activations"""
     import torch
     from synth import workloads as W
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
@@ -569,6 +570,19 @@ def profile_target(nv, target, launches):
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
+    if target == "rotate":
+        wl = W.generate("gdn_in_proj_8192x16384x5120", with_weight=False)
+        p = W.krpbh_params(wl.K, 512, seed=0)
+        perm, signs, Q = (torch.from_numpy(p[n]).cuda() for n in ("perm", "signs", "Q"))
+        xt = dev_bf16(wl.data["x_bf16"])
+        ac, as_ = nv.empty_packed(wl.M, wl.K, "cuda")
+        ag = torch.empty(1, dtype=torch.float32, device="cuda")
+        cx = torch.empty(wl.M, dtype=torch.float32, device="cuda")
+        for _ in range(launches):
+            nv.nvfp4_rotate_quantize(xt, perm, signs, Q, ac, as_, ag, cx)
+        torch.cuda.synchronize()
+        print(f"profile target rotate: {launches} calls (rotate+amax, rotate+quantize) on 8192 x 5120", flush=True)
+        return
     if target == "gdn":
         T = 8192
         hd = W.GDN_HEADS
@@ -663,7 +677,7 @@ def main():
     ap.add_argument("--decode-only", action="store_true", help="time only the decode GEMV (no JSON contract line)")
     ap.add_argument("--no-configs", action="store_true", help="skip the GDN-gates and MLP gate/up workloads")
     ap.add_argument("--configs-only", action="store_true", help="time only the GDN-gates and MLP gate/up workloads")
-    ap.add_argument("--profile-target", choices=["gemm", "quant", "decode", "gates", "requant", "mxgemm", "gdn"],
+    ap.add_argument("--profile-target", choices=["gemm", "quant", "decode", "gates", "requant", "mxgemm", "gdn", "rotate"],
                     help="for counter runs: a calibration copy, then a few launches of one kernel (no JSON line)")
     ap.add_argument("--launches", type=int, default=3)
     args = ap.parse_args()
