@@ -308,6 +308,38 @@ def test_gemm_big_tile_ragged(nv):
         P.assert_within_tolerance(P.y_to_f64(r["y"]), yref, bound, f"big tile linear={use_linear}")
 
 
+def _cut_k(wl, K):
+    """Keep the first K columns of X and W (a shorter reduction, same value mix)."""
+    wl.K = K
+    for key in ("x32", "x_bf16", "w32"):
+        if key in wl.data:
+            wl.data[key] = np.ascontiguousarray(wl.data[key][:, :K])
+    return wl
+
+
+@pytest.mark.parametrize("M,seg_end,K", [
+    (4100, [1200, 3000, 4500], 640),      # 17 x 18 = 306 tiles: workgroups with two tiles, ragged in M and N
+    (4352, [2176, 4352], 256),            # 289 tiles, four K steps
+])
+def test_gemm_big_tile_several_tiles_per_workgroup(nv, M, seg_end, K):
+    """More 256 x 256 tiles than compute units (a second round of workgroups), ragged
+    last tiles in both dimensions, a short K; sampled rows include every row of the
+    last row tile and sampled columns every column of the last column tile and the
+    segment boundaries."""
+    wl = W.generate("gdn_in_proj_8192x16384x5120", M=M, with_weight=False)
+    _cut_k(wl, K)
+    _shrink(wl, seg_end, sigma=[0.02, 0.05, 0.01][:len(seg_end)])
+    N = wl.N
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([rng.choice(M, 40, replace=False), np.arange((M - 1) // 256 * 256, M)]))
+    cols = np.unique(np.concatenate([rng.choice(N, 300, replace=False), np.arange((N - 1) // 256 * 256, N),
+                                     np.asarray(seg_end[:-1]) - 1, np.asarray(seg_end[:-1])]))
+    r = _run_layer(nv, wl, False, act_static=0.04)
+    yref, _, bound = _oracle_side(wl, r, act_static=0.04, rows=rows, cols=cols)
+    y = P.y_to_f64(r["y"])[rows][:, cols]
+    P.assert_within_tolerance(y, yref, bound, f"several tiles per workgroup M={M} N={N} K={K}")
+
+
 def _full_size_check(nv, name, seg_ratio=False, n_rows=24, n_cols=None, seed=5):
     """Full-size run in bench.py's launch configuration (quantize + GEMM, static
     activation scale from a dynamic pre-pass); the oracle checks sampled rows
