@@ -172,13 +172,18 @@ __global__ void k_fill(float* dst, int n, SegTable vals, int use_vals) {
 }
 
 
-// workgroups for `items` wave-iterations: enough to fill every CU several times
-int grid_for(uint64_t items) {
-  uint64_t g = (items + kWaves - 1) / kWaves;
-  const uint64_t cap = 256ull * 8ull;
-  if (g > cap) g = cap;
+// Workgroups for `items` wave-iterations of a grid-stride kernel: at most 2048
+// workgroups (8 per compute unit), and the waves evenly loaded (the same number of
+// iterations each, give or take one), so that no last round runs with a few waves
+// only: 10240 iterations (8192 rows of 5120) run as 5120 waves of two, not 8192
+// waves of which 2048 run a second one.
+uint64_t grid_for(uint64_t items) {
+  const uint64_t max_waves = 2048ull * kWaves;
+  const uint64_t per_wave = items > max_waves ? (items + max_waves - 1) / max_waves : 1;
+  const uint64_t waves = (items + per_wave - 1) / per_wave;
+  uint64_t g = (waves + kWaves - 1) / kWaves;
   if (g < 1) g = 1;
-  return (int)g;
+  return g;
 }
 
 }  // namespace
@@ -193,26 +198,30 @@ hipError_t launch_fill(float* dst, int n, const SegTable* vals, hipStream_t s) {
 
 hipError_t launch_amax_gscale(const void* x, InType t, int64_t rows, int64_t K, int64_t ld,
                               float* gscale_out, hipStream_t s) {
-  const uint64_t segs = (uint64_t)rows * (uint64_t)((K / 16 + 63) / 64);
-  const int grid = grid_for((segs + QU - 1) / QU);
-  if (t == InType::BF16)
-    hipLaunchKernelGGL(k_amax_gscale<InType::BF16>, dim3(grid), dim3(kThreads), 0, s, x, rows, K, ld, gscale_out);
-  else
-    hipLaunchKernelGGL(k_amax_gscale<InType::F32>, dim3(grid), dim3(kThreads), 0, s, x, rows, K, ld, gscale_out);
+  const uint64_t items = ((uint64_t)rows * (uint64_t)((K / 16 + 63) / 64) + QU - 1) / QU;
+  const unsigned grid = (unsigned)grid_for(items);
+  if (t == InType::BF16) {
+    hipLaunchKernelGGL(k_amax_gscale<InType::BF16>, dim3(grid), dim3(kThreads), 0, s, x, rows, K, ld,
+                       gscale_out);
+  } else {
+    hipLaunchKernelGGL(k_amax_gscale<InType::F32>, dim3(grid), dim3(kThreads), 0, s, x, rows, K, ld,
+                       gscale_out);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_quant_rows(const void* x, InType t, int64_t rows, int64_t K, int64_t ld,
                              const float* gvec, const SegTable& seg, uint8_t* codes, uint8_t* scales,
                              float* gcopy, hipStream_t s) {
-  const uint64_t segs = (uint64_t)rows * (uint64_t)((K / 16 + 63) / 64);
-  const int grid = grid_for((segs + QU - 1) / QU);
-  if (t == InType::BF16)
-    hipLaunchKernelGGL(k_quant_rows<InType::BF16>, dim3(grid), dim3(kThreads), 0, s, x, rows, K, ld, gvec, seg,
-                       codes, scales, gcopy);
-  else
-    hipLaunchKernelGGL(k_quant_rows<InType::F32>, dim3(grid), dim3(kThreads), 0, s, x, rows, K, ld, gvec, seg,
-                       codes, scales, gcopy);
+  const uint64_t items = ((uint64_t)rows * (uint64_t)((K / 16 + 63) / 64) + QU - 1) / QU;
+  const unsigned grid = (unsigned)grid_for(items);
+  if (t == InType::BF16) {
+    hipLaunchKernelGGL(k_quant_rows<InType::BF16>, dim3(grid), dim3(kThreads), 0, s, x, rows, K, ld, gvec,
+                       seg, codes, scales, gcopy);
+  } else {
+    hipLaunchKernelGGL(k_quant_rows<InType::F32>, dim3(grid), dim3(kThreads), 0, s, x, rows, K, ld, gvec,
+                       seg, codes, scales, gcopy);
+  }
   return hipGetLastError();
 }
 
