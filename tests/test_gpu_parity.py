@@ -586,3 +586,49 @@ def test_full_gdn_gates_fused_linear_sampled(nv, mode):
         P.assert_within_tolerance(P.y_to_f64(y[rsel]), yref, bound, f"gates fused {mode}")
     if len(outs) == 2:
         assert torch.equal(outs[0][0], outs[1][0])      # writing the codes does not change y
+
+
+# ----------------------------------------------------------------------------- degenerate input
+
+@pytest.mark.parametrize("M,N,seg_end,K,gate_heads,route", [
+    (4, 640, [320, 640], 1024, 0, "linear"),          # decode GEMV (fused quantize)
+    (300, 96, [48, 96], 512, 48, "linear"),           # skinny fused kernel with the gate epilogue
+    (600, 640, [256, 640], 512, 0, "two_stage"),      # quantizer + 256 x 256 GEMM
+])
+def test_all_zero_activation(nv, M, N, seg_end, K, gate_heads, route):
+    """An all-zero activation tensor (some entries -0.0) in dynamic mode: amax 0 gives
+    g = 0, every block scale byte 0 and codes that keep only the sign of zero; the
+    GEMM output is exactly 0 (the gate epilogue then gives its value at 0)."""
+    rng = np.random.default_rng(3)
+    x = np.zeros((M, K), dtype=np.float32)
+    x[rng.random((M, K)) < 0.3] = -0.0
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    xt = torch.from_numpy(x).cuda().to(torch.bfloat16)
+    wc, ws, wg = P.gpu_pack(nv, P.dev_x(w), seg_end)
+    gate = None
+    if gate_heads:
+        A_log = rng.uniform(-1.0, 2.7, gate_heads).astype(np.float32)
+        dt_bias = rng.uniform(-3.0, 3.0, gate_heads).astype(np.float32)
+        gate = (torch.from_numpy(A_log).cuda(), torch.from_numpy(dt_bias).cuda())
+    y = torch.full((M, N), 7.0, dtype=torch.float32 if gate_heads else torch.bfloat16, device="cuda")
+    ac, as_ = nv.empty_packed(M, K, "cuda")
+    gout = torch.full((1,), 5.0, dtype=torch.float32, device="cuda")
+    if route == "linear":
+        nv.nvfp4_w4a4_linear(xt, None, gout, wc, ws, seg_end, wg, y, gate=gate, a_codes_out=ac, a_scales_out=as_)
+    else:
+        nv.nvfp4_quantize_act(xt, None, ac, as_, gout)
+        nv.nvfp4_w4a4_gemm(ac, as_, gout, wc, ws, seg_end, wg, y, gate=gate)
+    torch.cuda.synchronize()
+    x64 = xt.float().cpu().numpy().astype(np.float64)
+    oac, oas, og = O.quantize_activation(x64)
+    assert og == 0.0 and gout.item() == 0.0
+    P.assert_bytes_equal(ac.cpu().numpy(), oac, "codes of an all-zero tensor")
+    P.assert_bytes_equal(as_.cpu().numpy(), oas, "scales of an all-zero tensor")
+    owc, ows, owg = O.pack_weight(w.astype(np.float64), seg_end)
+    yref, _, bound = P.oracle_reference(oac, oas, og, owc, ows, seg_end, owg, "f32" if gate_heads else "bf16",
+                                        gate=None if gate is None else (A_log, dt_bias))
+    got = P.y_to_f64(y)
+    if gate_heads:
+        P.assert_within_tolerance(got, yref, bound, "gate epilogue at y = 0")
+    else:
+        assert np.array_equal(got, np.zeros_like(got)), "GEMM of an all-zero activation is not exactly 0"
