@@ -61,11 +61,18 @@ __device__ __forceinline__ float lds_elem(const uint8_t* row, uint32_t idx) {
 template <InType T, int KB, bool QUANT>
 __global__ __launch_bounds__(64 * RQ_WAVES) void k_rotate(RotArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t rq_lds[];
+  // AMAX: the workgroup's largest |z| per segment (fp32 bits; non-negative values order
+  // as their bits), folded into the global maximum once per workgroup and segment
+  __shared__ uint32_t seg_amax[kMaxSeg];
   constexpr int ESZ = (T == InType::BF16) ? 2 : 4;
   constexpr int KD = KB * RQ_H;                                  // row length
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   uint8_t* row_lds = rq_lds + wave * KD * ESZ;
+  if constexpr (!QUANT) {
+    if ((int)threadIdx.x < a.seg.n) seg_amax[threadIdx.x] = 0u;
+    __syncthreads();
+  }
 
   // gather table: position s*512 + 8*lane + j reads element perm[...], sign in bit 15
   uint32_t po[KB * 4];
@@ -159,7 +166,7 @@ __global__ __launch_bounds__(64 * RQ_WAVES) void k_rotate(RotArgs a) {
         for (int j = 0; j < 8; ++j) am = __builtin_fmaxf(am, __builtin_fabsf(z[r][j]));
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) am = __builtin_fmaxf(am, __shfl_xor(am, off));
-      if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(a.gout + sgi), __float_as_uint(global_scale_from_amax(am)));
+      if (lane == 0) atomicMax(&seg_amax[sgi], __float_as_uint(am));
     } else {
       const float g = a.gvec[sgi];
       const ScaleConsts sc = scale_consts(g);
@@ -205,6 +212,13 @@ __global__ __launch_bounds__(64 * RQ_WAVES) void k_rotate(RotArgs a) {
       qz *= g;
       if (lane == 0) a.cbc[row] = qz > 0.0f ? zz / qz : 1.0f;
     }
+  }
+  if constexpr (!QUANT) {
+    // g = fp32(amax / 2688) is monotone in amax: the largest g is the g of the largest amax
+    __syncthreads();
+    if ((int)threadIdx.x < a.seg.n && seg_amax[threadIdx.x] != 0u)
+      atomicMax(reinterpret_cast<unsigned int*>(a.gout + threadIdx.x),
+                __float_as_uint(global_scale_from_amax(__uint_as_float(seg_amax[threadIdx.x]))));
   }
 }
 
