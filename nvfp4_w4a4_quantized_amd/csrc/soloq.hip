@@ -66,9 +66,15 @@ __global__ __launch_bounds__(64 * RQ_WAVES) void k_rotate(RotArgs a) {
   __shared__ uint32_t seg_amax[kMaxSeg];
   constexpr int ESZ = (T == InType::BF16) ? 2 : 4;
   constexpr int KD = KB * RQ_H;                                  // row length
+  // bf16 rows come into LDS by direct-to-LDS loads one row ahead of their use (two
+  // row buffers per wave, no registers held for them); fp32 rows (the offline weight
+  // rotation) are staged through registers into one buffer
+  constexpr bool DMA = (T == InType::BF16);
+  constexpr int NBUF = DMA ? 2 : 1;
+  constexpr int NCH = KD * ESZ / 1024;                           // 1 KiB pieces of a row
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  uint8_t* row_lds = rq_lds + wave * KD * ESZ;
+  uint8_t* const row_base = rq_lds + wave * NBUF * KD * ESZ;
   if constexpr (!QUANT) {
     if ((int)threadIdx.x < a.seg.n) seg_amax[threadIdx.x] = 0u;
     __syncthreads();
@@ -90,13 +96,42 @@ __global__ __launch_bounds__(64 * RQ_WAVES) void k_rotate(RotArgs a) {
   const float hs = 0.044194173824159216f;                       // fp32(1 / sqrt(512))
 
   const int64_t nwaves = (int64_t)gridDim.x * RQ_WAVES;
-  for (int64_t row = (int64_t)blockIdx.x * RQ_WAVES + wave; row < a.rows; row += nwaves) {
-    // stage the row in LDS (16-byte pieces)
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.x) + row * a.ldx * ESZ;
-    constexpr int NPC = KD * ESZ / 16;
-    for (int i = lane; i < NPC; i += 64)
-      *reinterpret_cast<u32x4*>(row_lds + 16 * i) = *reinterpret_cast<const u32x4*>(src + 16 * i);
-    __builtin_amdgcn_s_waitcnt(0xC07F);                          // lgkmcnt(0): this wave's LDS writes
+  // row r -> LDS: NCH loads of 16 bytes per lane (lane l's bytes at piece + 16 l), through
+  // a buffer descriptor whose base is the row (no 32-bit limit on the offset into x)
+  auto dma_row = [&](int64_t r, uint8_t* buf) {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.x) + r * a.ldx * ESZ;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), (short)0, KD * ESZ, 0x00020000);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(buf + 1024 * c), 16,
+                                               (uint32_t)(16 * lane), 1024 * c, 0, 0);
+  };
+  int64_t row = (int64_t)blockIdx.x * RQ_WAVES + wave;
+  int cur = 0;
+  if constexpr (DMA) {
+    if (row < a.rows) dma_row(row, row_base);
+  }
+  for (; row < a.rows; row += nwaves, cur ^= (NBUF - 1)) {
+    uint8_t* const row_lds = row_base + cur * KD * ESZ;
+    if constexpr (DMA) {
+      // the next row into the other buffer (read two rows ago: that gather has completed),
+      // then wait for this row's loads; the stores of the previous row, issued after
+      // them, are waited for too (long complete by then)
+      if (row + nwaves < a.rows) {
+        dma_row(row + nwaves, row_base + (cur ^ 1) * KD * ESZ);
+        wait_vmcnt<NCH>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    } else {
+      // stage the row in LDS (16-byte pieces)
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(a.x) + row * a.ldx * ESZ;
+      constexpr int NPC = KD * ESZ / 16;
+      for (int i = lane; i < NPC; i += 64)
+        *reinterpret_cast<u32x4*>(row_lds + 16 * i) = *reinterpret_cast<const u32x4*>(src + 16 * i);
+      __builtin_amdgcn_s_waitcnt(0xC07F);                        // lgkmcnt(0): this wave's LDS writes
+    }
     __builtin_amdgcn_wave_barrier();
 
     // gather with signs
@@ -225,7 +260,7 @@ __global__ __launch_bounds__(64 * RQ_WAVES) void k_rotate(RotArgs a) {
 template <InType T, int KB>
 hipError_t launch_kb(const RotArgs& a, bool quant, hipStream_t s) {
   constexpr int ESZ = (T == InType::BF16) ? 2 : 4;
-  const size_t lds = (size_t)RQ_WAVES * KB * RQ_H * ESZ;
+  const size_t lds = (size_t)RQ_WAVES * (T == InType::BF16 ? 2 : 1) * KB * RQ_H * ESZ;
   const int64_t want = (a.rows + RQ_WAVES - 1) / RQ_WAVES;
   const unsigned grid = (unsigned)(want < 1024 ? want : 1024);
   hipError_t e;
