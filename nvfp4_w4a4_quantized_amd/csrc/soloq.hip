@@ -27,6 +27,8 @@
 // lanes 2b, 2b+1 of one 512-block: its amax is a max over the lane pair.
 #include "kernel_common.hpp"
 
+#include <atomic>
+
 namespace nvfp4 {
 
 namespace {
@@ -257,12 +259,30 @@ __global__ __launch_bounds__(64 * RQ_WAVES) void k_rotate(RotArgs a) {
   }
 }
 
+// Compute units of the current device, looked up once per device.  The rotation
+// kernel holds one wave per SIMD (its registers), so one workgroup per compute unit
+// is resident; a grid of that many keeps every wave on its rows for the whole launch
+// (8 rows each at 8192 rows), which hides the next row's load behind the current one
+// for all but the first row of a wave.
+int cu_count() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 template <InType T, int KB>
 hipError_t launch_kb(const RotArgs& a, bool quant, hipStream_t s) {
   constexpr int ESZ = (T == InType::BF16) ? 2 : 4;
   const size_t lds = (size_t)RQ_WAVES * (T == InType::BF16 ? 2 : 1) * KB * RQ_H * ESZ;
   const int64_t want = (a.rows + RQ_WAVES - 1) / RQ_WAVES;
-  const unsigned grid = (unsigned)(want < 1024 ? want : 1024);
+  const int64_t cap = cu_count();
+  const unsigned grid = (unsigned)(want < cap ? want : cap);
   hipError_t e;
   if (quant) {
     e = lds_limit_once<&k_rotate<T, KB, true>>((int)lds);
