@@ -307,8 +307,8 @@ def time_config(nv, name, steps, warmup):
 
 def time_tiny(nv, calls=200):
     """The tiny linear (64 x 128 x 256, fp32 in and out, dynamic scales for both
-    operands): latency of one nvfp4_w4a4_linear call (amax pass + the fused skinny
-    kernel), HIP events around each call."""
+    operands): latency of one nvfp4_w4a4_linear call (one launch: the fused skinny
+    kernel takes the activation amax itself), HIP events around each call."""
     import torch
     from synth import workloads as W
     wl = W.generate("tiny_linear_64x128x256")
@@ -323,7 +323,7 @@ def time_tiny(nv, calls=200):
     for i in range(20):
         call(i)
     d = dist(event_times(call, calls))
-    return dict(workload=wl.name, mode="nvfp4_w4a4_linear, dynamic activation scale (amax pass + fused kernel)",
+    return dict(workload=wl.name, mode="nvfp4_w4a4_linear, dynamic activation scale (amax inside the fused kernel)",
                 latency_us={k: (round(v * 1e3, 2) if k != "n" else v) for k, v in d.items()},
                 bound="launch latency")
 

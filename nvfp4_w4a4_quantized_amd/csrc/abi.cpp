@@ -208,7 +208,10 @@ int32_t linear_impl(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_
   if (nvfp4::linear_skinny_fits(M, g.N, K)) {
     hipError_t e = hipSuccess;
     const float* g_used = gscale_in;
-    if (!gscale_in) {                      // dynamic mode: amax pass over x first
+    // dynamic mode: one workgroup (M tokens or fewer) takes the amax itself; more
+    // tokens run an amax pass over x first
+    const bool amax_in_kernel = !gscale_in && M <= nvfp4::linear_skinny_tokens_per_wg();
+    if (!gscale_in && !amax_in_kernel) {
       e = nvfp4::launch_fill(gscale_out, 1, nullptr, s);
       if (e == hipSuccess) e = nvfp4::launch_amax_gscale(x, in_type(x_dtype), M, K, ldx, gscale_out, s);
       if (e != hipSuccess) return hip_status(e, "nvfp4_w4a4_linear amax launch");
@@ -219,7 +222,7 @@ int32_t linear_impl(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_
     p.x_type = in_type(x_dtype);
     p.ldx = ldx;
     p.gscale_in = g_used;
-    p.gscale_out = gscale_in ? gscale_out : nullptr;
+    p.gscale_out = (gscale_in || amax_in_kernel) ? gscale_out : nullptr;
     p.a_codes_out = codes_out;
     p.a_scales_out = scales_out;
     p.g = g;

@@ -77,11 +77,13 @@ hipError_t launch_gemv_fused(const GemvArgs& a, hipStream_t s);
 // Whether the streaming decode GEMV handles this shape (else the LDS-f16 fallback).
 bool gemv_stream_fits(int64_t M, int64_t K, InType t);
 
-// skinny.hip: fused quantize + GEMM for N <= 128 (x read once).  gscale_in must be
-// a device pointer to the activation global scale (the caller runs the amax pass
-// first in dynamic mode); gscale_out (optional) receives a copy; a_codes_out /
-// a_scales_out optional.
+// skinny.hip: fused quantize + GEMM for N <= 128 (x read once).  gscale_in is a
+// device pointer to the activation global scale (the caller runs the amax pass first
+// in dynamic mode), or NULL when M <= linear_skinny_tokens_per_wg() (one workgroup:
+// the kernel takes the amax of x itself); gscale_out (optional) receives the scale
+// used; a_codes_out / a_scales_out optional.
 bool linear_skinny_fits(int64_t M, int64_t N, int64_t K);
+int64_t linear_skinny_tokens_per_wg();
 hipError_t launch_linear_skinny(const GemvArgs& a, hipStream_t s);
 
 // requant.hip: re-encode a packed weight [N][K] with per-segment global scales

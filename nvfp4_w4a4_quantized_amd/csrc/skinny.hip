@@ -118,7 +118,42 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_linear_skinny(GemvArgs p) {
   const int64_t m0 = (int64_t)blockIdx.x * SK_TM;
   const int64_t tok = m0 + wave * 16 + rr;
   const int64_t trow = tok < M ? tok : M - 1;                        // clamped: in bounds, never stored
-  const float g = *p.gscale_in;
+  // Global scale: the caller's, or (gscale_in NULL: dynamic mode with every token in
+  // this one workgroup) fp32(amax / 2688) of x taken here, 8 elements per step.
+  float g;
+  if (p.gscale_in != nullptr) {
+    g = *p.gscale_in;
+  } else {
+    __shared__ float red_am[SK_THREADS / 64];
+    const int64_t per_row = K / 8, n8 = M * per_row;
+    float am = 0.0f;
+    for (int64_t i = tid; i < n8; i += SK_THREADS) {
+      const int64_t rr8 = i / per_row, c8 = (i - rr8 * per_row) * 8;
+      if constexpr (T == InType::BF16) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.x) + rr8 * p.ldx + c8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(w[e] << 16)),
+                                                   __builtin_fabsf(__uint_as_float(w[e] & 0xFFFF0000u))));
+      } else {
+        const f32x4* xp = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.x) + rr8 * p.ldx + c8);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const f32x4 w = xp[hh];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(w[e]));
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) am = __builtin_fmaxf(am, __shfl_xor(am, off));
+    if (lane == 0) red_am[wave] = am;
+    __syncthreads();
+    am = red_am[0];
+#pragma unroll
+    for (int i = 1; i < SK_THREADS / 64; ++i) am = __builtin_fmaxf(am, red_am[i]);
+    g = global_scale_from_amax(am);
+  }
   const ScaleConsts sc = scale_consts(g);
   if (blockIdx.x == 0 && tid == 0 && p.gscale_out != nullptr) *p.gscale_out = g;
 
@@ -284,7 +319,11 @@ bool linear_skinny_fits(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_linear_skinny(const GemvArgs& p, hipStream_t s) {
+  // in-kernel dynamic scale only when one workgroup holds every token
+  if (p.gscale_in == nullptr && p.g.M > SK_TM) return hipErrorInvalidValue;
   return p.x_type == InType::BF16 ? launch_epi<InType::BF16>(p, s) : launch_epi<InType::F32>(p, s);
 }
+
+int64_t linear_skinny_tokens_per_wg() { return SK_TM; }
 
 }  // namespace nvfp4
