@@ -465,6 +465,7 @@ def _skinny_case(M, N, seg_end, K, xdt, seed, gate_heads=0, y_dtype="bf16"):
     (129, 128, [64, 128], 512, "bf16", 0, "bf16"),     # four column tiles, two segments
     (200, 40, [8, 40], 768, "f32", 0, "f32"),          # three chunks, fp32 in and out
     (9, 96, [48, 96], 1024, "bf16", 48, "f32"),        # just above the decode GEMV's token limit
+    (128, 96, [48, 96], 5120, "bf16", 48, "f32"),      # the most tokens one workgroup takes (dynamic: amax in-kernel)
 ])
 @pytest.mark.parametrize("mode", ["static", "dynamic"])
 @pytest.mark.parametrize("codes_out", [True, False])
