@@ -427,73 +427,120 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   static_assert(EPI != EPI_GATE, "the gate epilogue runs in the 128x128-tile kernel");
   constexpr int ESZ = (EPI == EPI_BF16) ? 2 : 4;
   const int64_t extent = ((a.M - 1) * a.ldy + a.N) * ESZ;
-  // per-row factors of this lane's 64 rows (rows past M read row M - 1, never stored)
-  float rsc[4][16];
   if constexpr (RC) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+    // With per-row factors the epilogue goes row block by row block, holding the 16 row
+    // factors of one block at a time (all 64 in registers at once spilled to scratch):
+    // y = (acc * fp32(alpha_n * col_n)) * row_m, each product rounded once.
+    auto row_factors = [&](int i, float rs[16]) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        rsc[i][r] = a.row_scale[min<int64_t>(m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3), a.M - 1)];
-  }
-  auto scaled = [&](int i, int j, int r) {
-    const float v = acc[i][j][r] * alpha[j];
-    if constexpr (RC) return v * rsc[i][r];
-    else return v;
-  };
-  if (m0 + GBM <= a.M && n0 + GBN <= a.N && extent < (int64_t(1) << 32) && (a.ldy % 2) == 0) {
-    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, (int)(uint32_t)extent, 0x00020000);
-    const uint32_t ldyb = (uint32_t)a.ldy * ESZ;
-    // wave-uniform (wm, wn are per wave); readfirstlane tells the compiler so
-    const uint32_t tile_off = __builtin_amdgcn_readfirstlane((uint32_t)(m0 + wm * 128) * ldyb + (uint32_t)(n0 + wn * 128) * ESZ);
-    if constexpr (EPI == EPI_BF16) {
-      const bool odd = (li & 1) != 0;
-      const uint32_t voff = (uint32_t)(4 * h) * ldyb + (uint32_t)li * 2 + (odd ? ldyb - 2 : 0u);
-      const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+        rs[r] = a.row_scale[min<int64_t>(m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3), a.M - 1)];
+    };
+    if (m0 + GBM <= a.M && n0 + GBN <= a.N && extent < (int64_t(1) << 32) && (a.ldy % 2) == 0) {
+      const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, (int)(uint32_t)extent, 0x00020000);
+      const uint32_t ldyb = (uint32_t)a.ldy * ESZ;
+      const uint32_t tile_off = __builtin_amdgcn_readfirstlane((uint32_t)(m0 + wm * 128) * ldyb + (uint32_t)(n0 + wn * 128) * ESZ);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int i = 0; i < 4; ++i) {
+        float rs[16];
+        row_factors(i, rs);
+        if constexpr (EPI == EPI_BF16) {
+          const bool odd = (li & 1) != 0;
+          const uint32_t voff = (uint32_t)(4 * h) * ldyb + (uint32_t)li * 2 + (odd ? ldyb - 2 : 0u);
+          const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int p = 0; p < 8; ++p) {
-            typedef float f32x2 __attribute__((ext_vector_type(2)));
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            const f32x2 v = {scaled(i, j, 2 * p), scaled(i, j, 2 * p + 1)};
-            const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-            const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp((int)pk, (int)pk, 0xB1, 0xF, 0xF, false);
-            const uint32_t word = __builtin_amdgcn_perm(nb, pk, sel);
-            const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (p >> 1) + 2 * (p & 1)) * ldyb + (uint32_t)(j * 64);
-            __builtin_amdgcn_raw_buffer_store_b32(word, yr, voff, soff, 0);
-          }
-    } else {
-      const uint32_t voff = (uint32_t)(4 * h) * ldyb + (uint32_t)li * 4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldyb + (uint32_t)(j * 128);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(scaled(i, j, r)), yr, voff, soff, 0);
-          }
-    }
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + wn * 128 + j * 32 + li;
-    const bool n_ok = n < a.N;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if constexpr (RC) {
-          if (n_ok && m < a.M) store_out_rc<EPI>(a, m, n, acc[i][j][r], alpha[j], rsc[i][r]);
+            for (int p = 0; p < 8; ++p) {
+              typedef float f32x2 __attribute__((ext_vector_type(2)));
+              typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+              const f32x2 v = {(acc[i][j][2 * p] * alpha[j]) * rs[2 * p], (acc[i][j][2 * p + 1] * alpha[j]) * rs[2 * p + 1]};
+              const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+              const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp((int)pk, (int)pk, 0xB1, 0xF, 0xF, false);
+              const uint32_t word = __builtin_amdgcn_perm(nb, pk, sel);
+              const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (p >> 1) + 2 * (p & 1)) * ldyb + (uint32_t)(j * 64);
+              __builtin_amdgcn_raw_buffer_store_b32(word, yr, voff, soff, 0);
+            }
         } else {
-          if (n_ok && m < a.M) store_out<EPI>(a, m, n, acc[i][j][r], alpha[j]);
+          const uint32_t voff = (uint32_t)(4 * h) * ldyb + (uint32_t)li * 4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldyb + (uint32_t)(j * 128);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((acc[i][j][r] * alpha[j]) * rs[r]), yr, voff, soff, 0);
+            }
         }
       }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float rs[16];
+      row_factors(i, rs);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + wn * 128 + j * 32 + li;
+        const bool n_ok = n < a.N;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (n_ok && m < a.M) store_out_rc<EPI>(a, m, n, acc[i][j][r], alpha[j], rs[r]);
+        }
+      }
+    }
+  } else {
+    auto scaled = [&](int i, int j, int r) { return acc[i][j][r] * alpha[j]; };
+    if (m0 + GBM <= a.M && n0 + GBN <= a.N && extent < (int64_t(1) << 32) && (a.ldy % 2) == 0) {
+      const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, (int)(uint32_t)extent, 0x00020000);
+      const uint32_t ldyb = (uint32_t)a.ldy * ESZ;
+      // wave-uniform (wm, wn are per wave); readfirstlane tells the compiler so
+      const uint32_t tile_off = __builtin_amdgcn_readfirstlane((uint32_t)(m0 + wm * 128) * ldyb + (uint32_t)(n0 + wn * 128) * ESZ);
+      if constexpr (EPI == EPI_BF16) {
+        const bool odd = (li & 1) != 0;
+        const uint32_t voff = (uint32_t)(4 * h) * ldyb + (uint32_t)li * 2 + (odd ? ldyb - 2 : 0u);
+        const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+              typedef float f32x2 __attribute__((ext_vector_type(2)));
+              typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+              const f32x2 v = {scaled(i, j, 2 * p), scaled(i, j, 2 * p + 1)};
+              const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+              const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp((int)pk, (int)pk, 0xB1, 0xF, 0xF, false);
+              const uint32_t word = __builtin_amdgcn_perm(nb, pk, sel);
+              const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (p >> 1) + 2 * (p & 1)) * ldyb + (uint32_t)(j * 64);
+              __builtin_amdgcn_raw_buffer_store_b32(word, yr, voff, soff, 0);
+            }
+      } else {
+        const uint32_t voff = (uint32_t)(4 * h) * ldyb + (uint32_t)li * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldyb + (uint32_t)(j * 128);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(scaled(i, j, r)), yr, voff, soff, 0);
+            }
+      }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + wn * 128 + j * 32 + li;
+      const bool n_ok = n < a.N;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (n_ok && m < a.M) store_out<EPI>(a, m, n, acc[i][j][r], alpha[j]);
+        }
+    }
   }
 }
 
