@@ -460,7 +460,7 @@ __global__ __launch_bounds__(GW_THREADS, 1) void k_gemv_ws(GemvArgs p) {
     const u32x4* wc = reinterpret_cast<const u32x4*>(a.w_codes + (nrow < N ? nrow : N - 1) * (K >> 1) +
                                                      (kbase >> 1) + 16 * q);   // row clamped: in bounds, never stored
     u32x4 codes[NL];
-    lds_sync();                                                  // barrier X (x has landed)
+    lds_sync();                                                  // barrier X (x issued)
 #pragma unroll
     for (int i = 0; i < NA; ++i) codes[i] = __builtin_nontemporal_load(wc + 4 * i);
     if (dynamic) lds_sync();                                     // barrier A (amax partials)
@@ -643,6 +643,295 @@ __global__ __launch_bounds__(GW_THREADS, 1) void k_gemv_ws(GemvArgs p) {
   __syncthreads();                                               // barrier C
 }
 
+
+// ---------------------------------------------------------------------------------
+// Fused decode GEMV for M <= 4 tokens, K % 512 == 0, 2 <= K / 512 <= 16 (the decode
+// shape 4 x 16384 x 5120 among them).  Workgroup = 64 weight rows, one wave per
+// 512-element K slice.  MFMA 4x4x4 f16 (16 blocks): block b = lane >> 2 takes the
+// slice's K positions 32 b .. 32 b + 31; A lane (b, i = lane & 3) = weight row i of
+// the current group of four rows, B lane (b, j = lane & 3) = token j, so four tokens
+// fill the B columns with no padding.  Lane layout of this instruction (measured on
+// the GPU with one-hot operands): A[i][k] of block b in lane 4 b + i, element k;
+// B[k][j] in lane 4 b + j, element k; D[i][j] in lane 4 b + j, register i.
+//  * weight: load r (0..15) brings rows 4 r .. 4 r + 3: lane (b, i) reads the 16
+//    bytes of row 4 r + i at chunk b of the slice, so each instruction reads four
+//    rows' 256 bytes as whole cache lines (the 16-rows-by-64-bytes pattern of the
+//    other decode kernels reads half lines and streams about 25% slower).
+//  * x: lane (b, j) loads token j's 32 elements of chunk b, quantizes them in the lane
+//    (two whole 16-element blocks, the exact quantizer of the stand-alone kernel) and
+//    keeps them as f16 e2m1 * s for all 16 row groups: no LDS and, with a calibrated
+//    scale, no barrier before the stream is consumed.
+//  * weight scales: the slice's 32 bytes of each of the 64 rows go to LDS by two
+//    direct-to-LDS loads per wave, read by the same wave only.
+//  * end: a butterfly over the 16 blocks (lane bits 5, 4, 3, 2) leaves lane (b, j)
+//    with rows 4 b .. 4 b + 3 of token j; the slices are added through LDS in slice
+//    order; epilogue.
+// ---------------------------------------------------------------------------------
+constexpr int G4_RG = 16;                // groups of four weight rows per workgroup (64 rows)
+// Weight loads in flight per lane in the main loop, and how many of them are issued
+// before the x quantization.  Measured at 4 x 16384 x 5120: loads issued ahead of the
+// quantization stall the wave at issue once the memory system stops taking them, and
+// the quantization waits behind them (8 ahead: 14.0 us, 12: 15.0, 16: 19.7; 2-6 ahead
+// of the quantization with 8 in the loop are within noise of each other).
+constexpr int G4_NA = 8;
+constexpr int G4_NA0 = 4;
+constexpr int G4_MAXW = 16;              // K / 512 <= 16
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+__host__ __device__ constexpr int64_t g4_lds_bytes(int nw, int rg) { return (int64_t)nw * 4 * rg * (32 + 16) + 64; }
+
+template <InType T> struct G4X;                       // 32 elements of one token
+template <> struct G4X<InType::BF16> { u32x4 q[4]; };
+template <> struct G4X<InType::F32> { f32x4 q[8]; };
+
+template <InType T>
+__device__ __forceinline__ void g4x_load(const void* base, int64_t elem_off, G4X<T>& r) {
+  if constexpr (T == InType::BF16) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem_off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.q[i] = p[i];
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + elem_off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.q[i] = p[i];
+  }
+}
+
+template <InType T>
+__device__ __forceinline__ void g4x_unpack(const G4X<T>& r, float v[32]) {
+  if constexpr (T == InType::BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * i + 2 * e] = __uint_as_float(r.q[i][e] << 16);
+        v[8 * i + 2 * e + 1] = __uint_as_float(r.q[i][e] & 0xFFFF0000u);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * i + e] = r.q[i][e];
+  }
+}
+
+__device__ __forceinline__ f32x4 shfl_xor4(f32x4 v, int m) {
+  f32x4 r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r[c] = __shfl_xor(v[c], m);
+  return r;
+}
+
+// One butterfly step over lane bit `bit`: of the 2h row-group accumulators in[],
+// lanes with the bit clear keep the first h and add their partner's, lanes with the
+// bit set keep the second h.
+template <int H>
+__device__ __forceinline__ void g4_fold(const f32x4* in, f32x4* out, int lane, int bit) {
+  const bool hi = (lane & bit) != 0;
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const f32x4 mine = hi ? in[H + k] : in[k];
+    const f32x4 give = hi ? in[k] : in[H + k];
+    out[k] = mine + shfl_xor4(give, bit);
+  }
+}
+
+// The same step over lane bit 5 (bit 4) by v_permlane32_swap (v_permlane16_swap): the
+// swap of the upper half of in[k] with the lower half of in[H + k] (of the odd 16-lane
+// rows of in[k] with the even rows of in[H + k]) leaves every lane holding its own kept
+// value and its partner's in the two results, with no LDS round trip.
+template <int H>
+__device__ __forceinline__ void g4_fold_swap32(const f32x4* in, f32x4* out) {
+#pragma unroll
+  for (int k = 0; k < H; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(in[k][c]), __float_as_uint(in[H + k][c]), false, false);
+      out[k][c] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
+
+template <int H>
+__device__ __forceinline__ void g4_fold_swap16(const f32x4* in, f32x4* out) {
+#pragma unroll
+  for (int k = 0; k < H; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(in[k][c]), __float_as_uint(in[H + k][c]), false, false);
+      out[k][c] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
+
+template <InType T, int EPI>
+__global__ __launch_bounds__(64 * G4_MAXW) void k_gemv_k4(GemvArgs p) {
+  constexpr int RG = G4_RG;                                      // groups of four weight rows
+  constexpr int ROWS = 4 * RG;                                   // weight rows per workgroup
+  static_assert(G4_NA0 >= 1 && G4_NA0 <= RG && G4_NA >= G4_NA0, "load look-ahead");
+  extern __shared__ __attribute__((aligned(16))) uint8_t g4_lds[];
+  const GemmArgs& a = p.g;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;                                        // K slice
+  const int nw = (int)(a.K >> 9);
+  const int64_t M = a.M, K = a.K, N = a.N;
+  const int64_t n0 = (int64_t)blockIdx.x * ROWS;
+  const int b = lane >> 2, i4 = lane & 3;
+  uint8_t* const sc_lds = g4_lds + w * (32 * ROWS);             // [ROWS rows][32 scale bytes]
+  float* const part = reinterpret_cast<float*>(g4_lds + nw * 32 * ROWS);   // [nw][ROWS rows][4 tokens]
+  float* const red = part + nw * 4 * ROWS;                       // [nw] amax of each slice
+  const bool dynamic = (p.gscale_in == nullptr);
+  // calibrated global scale (from an always-valid address in dynamic mode, unused there)
+  const float g_in = *(dynamic ? a.w_seg_gscale : p.gscale_in);
+  // the epilogue operands of this thread's output row (threads t < 4 ROWS take row
+  // t % ROWS in the last step), loaded now so that the tail has no memory round trip
+  const int64_t n_ep = min<int64_t>(n0 + (tid % ROWS), N - 1);
+  const float w_seg_g = a.w_seg_gscale[seg_of_col(a.seg, n_ep)];
+  float ep_alog = 0.0f, ep_db = 0.0f;
+  if constexpr (EPI == EPI_GATE) {
+    const int64_t nh = n_ep < a.gate.n_heads ? n_ep : 0;
+    ep_alog = a.gate.A_log[nh];
+    ep_db = a.gate.dt_bias[nh];
+  }
+
+  // (1) x: token j = i4, elements 512 w + 32 b .. +31; tokens past M re-read token 0
+  // (in bounds) and are zeroed below
+  const int64_t kx = 512 * (int64_t)w + 32 * b;
+  G4X<T> xr;
+  g4x_load<T>(p.x, (i4 < M ? i4 : 0) * p.ldx + kx, xr);
+  asm volatile("" ::: "memory");
+  // (2) the slice's weight scales: row r's 32 bytes at sc_lds + 32 r; load h covers
+  // rows 32 h .. 32 h + 31 (rows past N clamp their source: in bounds, never stored)
+  {
+    const int64_t kb = K >> 4;
+#pragma unroll
+    for (int h = 0; h < RG / 8; ++h) {
+      const int64_t row = min<int64_t>(n0 + 32 * h + (lane >> 1), N - 1);
+      __builtin_amdgcn_global_load_lds(a.w_scales + row * kb + 32 * w + 16 * (lane & 1), sc_lds + 1024 * h, 16, 0, 0);
+    }
+  }
+  asm volatile("" ::: "memory");
+  // (3) the weight stream: load r = row 4 r + i4, chunk b of the slice
+  const int64_t kh = K >> 1;
+  const uint8_t* const wbase = a.w_codes + 256 * (int64_t)w + 16 * b;
+  auto wptr = [&](int r) {
+    const int64_t row = min<int64_t>(n0 + 4 * r + i4, N - 1);
+    return reinterpret_cast<const u32x4*>(wbase + row * kh);
+  };
+  u32x4 codes[RG];
+#pragma unroll
+  for (int r = 0; r < G4_NA0; ++r) codes[r] = __builtin_nontemporal_load(wptr(r));
+
+  // (4) global scale and the quantization of the lane's two blocks of x
+  wait_vmcnt<G4_NA0 + RG / 8>();                                 // x has landed
+  float v[32];
+  g4x_unpack<T>(xr, v);
+#pragma unroll
+  for (int e = 0; e < 32; ++e) v[e] = (i4 < M) ? v[e] : 0.0f;
+  float g = g_in;
+  if (dynamic) {
+    float am = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(v[e]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) am = __builtin_fmaxf(am, __shfl_xor(am, off));
+    if (lane == 0) red[w] = am;
+    lds_sync();
+    am = red[0];
+    for (int k = 1; k < nw; ++k) am = __builtin_fmaxf(am, red[k]);
+    g = global_scale_from_amax(am);
+  }
+  const ScaleConsts sc = scale_consts(g);
+  uint32_t sb[2], qw[4];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    float am = __builtin_fabsf(v[16 * blk]);
+#pragma unroll
+    for (int e = 1; e < 16; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(v[16 * blk + e]));
+    sb[blk] = block_scale_byte(am, sc);
+    quant16(v + 16 * blk, sb[blk], g, qw + 2 * blk);
+  }
+  // B operand of step t (0..7): the lane's elements 4 t .. 4 t + 3
+  f16x4 xb[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const f16x8 dd = decode8_f16(qw[d], scale_f16x2(sb[d >> 1]));
+    xb[2 * d] = f16x4{dd[0], dd[1], dd[2], dd[3]};
+    xb[2 * d + 1] = f16x4{dd[4], dd[5], dd[6], dd[7]};
+  }
+  wait_vmcnt<G4_NA0>();                                          // the scale loads have landed
+
+  // (5) main loop: row group r, MFMA steps t = 0..7 (elements 4 t .. 4 t + 3 of the
+  // lane's 32; block 2 b for t < 4, 2 b + 1 after)
+  f32x4 acc[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    // loads up to r + G4_NA - 1 in flight (at r = 0 the ones not issued before the
+    // quantization, then one per row group)
+    constexpr int lo0 = G4_NA0;
+#pragma unroll
+    for (int k = (r == 0 ? lo0 : min(RG, max(G4_NA0, r - 1 + G4_NA))); k < min(RG, max(G4_NA0, r + G4_NA)); ++k)
+      codes[k] = __builtin_nontemporal_load(wptr(k));
+    __builtin_amdgcn_sched_barrier(0);    // keep the loads here: the scheduler would sink them to their use
+    const f16x2 sp = scale_pair_f16(*reinterpret_cast<const uint16_t*>(sc_lds + 32 * (4 * r + i4) + 2 * b));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {                                // dword d: steps 2 d, 2 d + 1
+      const f16x2 s2 = bcast(sp, d >> 1);
+      const uint32_t dw = codes[r][d];
+      const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(dw, 1.0f, 0) * s2;
+      const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(dw, 1.0f, 1) * s2;
+      const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(dw, 1.0f, 2) * s2;
+      const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(dw, 1.0f, 3) * s2;
+      acc[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(f16x4{p0[0], p0[1], p1[0], p1[1]}, xb[2 * d], acc[r], 0, 0, 0);
+      acc[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(f16x4{p2[0], p2[1], p3[0], p3[1]}, xb[2 * d + 1], acc[r], 0, 0, 0);
+    }
+  }
+
+  // (6) the optional outputs of workgroup 0 (after the stream: a store before it would
+  // make the compiler wait for the stream's loads)
+  if (blockIdx.x == 0) {
+    if (tid == 0 && p.gscale_out) *p.gscale_out = g;
+    if (p.a_codes_out != nullptr && i4 < M) {
+      *reinterpret_cast<u32x4*>(p.a_codes_out + i4 * (K >> 1) + 256 * w + 16 * b) = u32x4{qw[0], qw[1], qw[2], qw[3]};
+      *reinterpret_cast<uint16_t*>(p.a_scales_out + i4 * (K >> 4) + 32 * w + 2 * b) = (uint16_t)(sb[0] | (sb[1] << 8));
+    }
+  }
+
+  // (7) sum over the 16 blocks: lane (b, j) ends with row group b of token j,
+  // register i = row 4 b + i
+  f32x4 h8[8], h4[4], h2[2], h1[1];
+  g4_fold_swap32<8>(acc, h8);
+  g4_fold_swap16<4>(h8, h4);
+  g4_fold<2>(h4, h2, lane, 8);
+  g4_fold<1>(h2, h1, lane, 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[w * 4 * ROWS + (4 * b + i) * 4 + i4] = h1[0][i];
+  lds_sync();
+
+  // (8) add the slices in order, epilogue (the store_out arithmetic with the operands
+  // loaded at the start): thread t -> row t % ROWS (the same for every t of a thread,
+  // as the block size is a multiple of ROWS), token t / ROWS
+  for (int t = tid; t < 4 * ROWS; t += 64 * nw) {
+    const int rr = t % ROWS, j = t / ROWS;
+    const int64_t n = n0 + rr;
+    if (j < M && n < N) {
+      float s = part[rr * 4 + j];
+      for (int k = 1; k < nw; ++k) s += part[k * 4 * ROWS + rr * 4 + j];
+      float v = s * (g * w_seg_g);
+      if constexpr (EPI == EPI_GATE) {
+        v = n < a.gate.n_heads ? -expf(ep_alog) * softplus_f32(v + ep_db) : sigmoid_f32(v);
+      }
+      if constexpr (EPI == EPI_BF16) {
+        reinterpret_cast<uint16_t*>(a.y)[j * a.ldy + n] = (uint16_t)f32_to_bf16_bits(v);
+      } else {
+        reinterpret_cast<float*>(a.y)[j * a.ldy + n] = v;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 size_t gemv_lds_bytes(int64_t M, int64_t K) { return (size_t)M * (size_t)K * 2; }
@@ -691,7 +980,27 @@ bool gemv_stream_fits(int64_t M, int64_t K, InType t) {
          (t == InType::BF16 || chunks_per_thread <= 5) && gs_lds_bytes(M, K) <= 152 * 1024;
 }
 
+static bool gemv_k4_fits(int64_t M, int64_t K) {
+  return M >= 1 && M <= 4 && K % 512 == 0 && K / 512 >= 2 && K / 512 <= G4_MAXW;
+}
+
+template <InType T>
+static hipError_t launch_k4(const GemvArgs& p, hipStream_t s) {
+  const int nw = (int)(p.g.K / 512);
+  const unsigned grid = (unsigned)((p.g.N + 4 * G4_RG - 1) / (4 * G4_RG));
+  const size_t lds = (size_t)g4_lds_bytes(nw, G4_RG);
+  if (p.g.gate.n_heads > 0)
+    hipLaunchKernelGGL((k_gemv_k4<T, EPI_GATE>), dim3(grid), dim3(64 * nw), lds, s, p);
+  else if (p.g.y_type == OutType::BF16)
+    hipLaunchKernelGGL((k_gemv_k4<T, EPI_BF16>), dim3(grid), dim3(64 * nw), lds, s, p);
+  else
+    hipLaunchKernelGGL((k_gemv_k4<T, EPI_F32>), dim3(grid), dim3(64 * nw), lds, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv_fused(const GemvArgs& p, hipStream_t s) {
+  if (gemv_k4_fits(p.g.M, p.g.K))
+    return p.x_type == InType::BF16 ? launch_k4<InType::BF16>(p, s) : launch_k4<InType::F32>(p, s);
   if (gemv_ws_fits(p.g.M, p.g.K, p.x_type)) {
     const unsigned grid = (unsigned)((p.g.N + GS_ROWS - 1) / GS_ROWS);
     const size_t lds = (size_t)gw_lds_bytes(p.g.M, p.g.K, p.x_type == InType::F32);

@@ -480,7 +480,10 @@ def test_linear_skinny_fused(nv, M, N, seg_end, K, xdt, gate_heads, y_dtype, mod
     (4, 96, [48, 96], 5120, "bf16", 48, "f32"),        # decode GEMV with the gate epilogue
     (1, 1000, [300, 1000], 2048, "f32", 0, "f32"),     # one token, fp32 in and out, ragged N
     (8, 520, [256, 520], 1024, "bf16", 0, "bf16"),     # eight tokens, ragged last workgroup
-    (3, 200, [200], 1536, "bf16", 0, "bf16"),          # K % 1024 != 0: the other decode kernel
+    (3, 200, [200], 1536, "bf16", 0, "bf16"),          # three tokens, three 512-element K slices
+    (6, 200, [200], 1536, "bf16", 0, "bf16"),          # K % 1024 != 0 with more than four tokens
+    (4, 130, [64, 130], 8192, "bf16", 0, "bf16"),      # sixteen K slices (the most), ragged N, two segments
+    (2, 64, [64], 1024, "f32", 0, "f32"),              # two K slices (the fewest), fp32 in and out
 ])
 @pytest.mark.parametrize("mode", ["static", "dynamic"])
 @pytest.mark.parametrize("codes_out", [True, False])
