@@ -494,6 +494,42 @@ def test_linear_decode_fused(nv, M, N, seg_end, K, xdt, gate_heads, y_dtype, mod
     _check_linear(nv, M, N, seg_end, K, xdt, gate_heads, y_dtype, mode, codes_out, "decode")
 
 
+@pytest.mark.parametrize("M,N,K,xdt", [
+    (3, 200, 2048, "bf16"),     # the 4x4x4 decode kernel (four K slices)
+    (6, 130, 1024, "bf16"),     # the two-role decode kernel (more than four tokens)
+    (2, 64, 1536, "f32"),       # the 4x4x4 decode kernel, fp32 rows
+    (40, 96, 512, "bf16"),      # the fused skinny kernel
+])
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_linear_fused_strided_x(nv, M, N, K, xdt, mode):
+    """The fused paths of nvfp4_w4a4_linear on x rows longer than their data (a column
+    slice of a wider tensor, ldx = K + 64): codes bit-exact, outputs within the GEMM
+    tolerance, against the oracle on the slice."""
+    rng = np.random.default_rng(M * 131 + K)
+    full = rng.standard_normal((M, K + 64)).astype(np.float32)
+    full[:, rng.choice(K, max(1, K // 100), replace=False)] *= 40
+    bits = W._to_bf16_bits(full) if xdt == "bf16" else None
+    xv = W.bf16_bits_to_f32(bits) if xdt == "bf16" else full
+    xt = P.dev_x(xv, bits)[:, :K]
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    seg_end = [N // 2, N]
+    wc, ws, wg = P.gpu_pack(nv, P.dev_x(w), seg_end, None)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    act = 0.0391 if mode == "static" else None
+    gin = None if act is None else torch.tensor([act], dtype=torch.float32, device="cuda")
+    gout = torch.empty(1, dtype=torch.float32, device="cuda")
+    ac, as_ = nv.empty_packed(M, K, "cuda")
+    nv.nvfp4_w4a4_linear(xt, gin, gout, wc, ws, seg_end, wg, y, a_codes_out=ac, a_scales_out=as_)
+    torch.cuda.synchronize()
+    oc, os_, og = O.quantize_activation(P.x64_of(xv[:, :K]), None if act is None else np.float32(act))
+    owc, ows, owg = O.pack_weight(w.astype(np.float64), seg_end)
+    assert np.float32(gout.item()) == og
+    P.assert_bytes_equal(ac.cpu().numpy(), oc, "activation codes")
+    P.assert_bytes_equal(as_.cpu().numpy(), os_, "activation scales")
+    yref, _, bound = P.oracle_reference(oc, os_, og, owc, ows, seg_end, owg, "bf16")
+    P.assert_within_tolerance(P.y_to_f64(y), yref, bound, f"strided x M={M} N={N} K={K} {xdt} {mode}")
+
+
 def _check_linear(nv, M, N, seg_end, K, xdt, gate_heads, y_dtype, mode, codes_out, what):
     wl = _skinny_case(M, N, seg_end, K, xdt, seed=M * 31 + N * 7 + K, gate_heads=gate_heads, y_dtype=y_dtype)
     act = 0.0457 if mode == "static" else None
