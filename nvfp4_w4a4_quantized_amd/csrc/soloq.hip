@@ -21,8 +21,9 @@
 // Layout: one wave = one row at a time (waves loop over rows).  The row of x is staged
 // in LDS for the gather.  Lane l holds positions 8l .. 8l+7 of every h = 512 block, so
 // the butterflies of distance 1, 2, 4 stay in the lane and those of distance 8 .. 256
-// pair lane l with lane l ^ (distance / 8): the lower lane forms v + p, the upper p - v,
-// as fma(+-1, v, p) (exact sign, one rounding).  The cross-block mix is in the lane
+// pair lane l with lane l ^ (distance / 8), whose value comes by DPP or a permlane swap
+// (no LDS round trip): the lower lane forms v + p, the upper p - v, as fma(+-1, v, p)
+// (exact sign, one rounding).  The cross-block mix is in the lane
 // (the same positions of every block).  An NVFP4 block (16 consecutive positions) is
 // lanes 2b, 2b+1 of one 512-block: its amax is a max over the lane pair.
 #include "kernel_common.hpp"
@@ -57,6 +58,33 @@ __device__ __forceinline__ float lds_elem(const uint8_t* row, uint32_t idx) {
     return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[idx] << 16);
   } else {
     return reinterpret_cast<const float*>(row)[idx];
+  }
+}
+
+// The value of lane l ^ m (m = 1 .. 32, a constant after unrolling), in VALU: DPP quad
+// permutations for m = 1, 2; row rotations by 12 and 4 for m = 4 (l + 4 for lanes with
+// bit 2 clear, l - 4 for the others); a rotation by 8 within the 16-lane row for m = 8;
+// v_permlane16_swap / v_permlane32_swap of the value with itself for m = 16, 32 (the two
+// results hold the lower and the upper row's / half's value).
+__device__ __forceinline__ float lane_xor(float v, int m, int lane) {
+  const int b = __float_as_int(v);
+  switch (m) {
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));
+    case 4: {
+      const int up = __builtin_amdgcn_update_dpp(0, b, 0x12C, 0xF, 0xF, false);    // row_ror:12
+      const int dn = __builtin_amdgcn_update_dpp(0, b, 0x124, 0xF, 0xF, false);    // row_ror:4
+      return __int_as_float((lane & 4) ? dn : up);
+    }
+    case 8: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, false));   // row_ror:8
+    case 16: {
+      const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+      return __uint_as_float((lane & 16) ? r[0] : r[1]);
+    }
+    default: {
+      const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+      return __uint_as_float((lane & 32) ? r[0] : r[1]);
+    }
   }
 }
 
@@ -165,12 +193,13 @@ __global__ __launch_bounds__(64 * RQ_WAVES) void k_rotate(RotArgs a) {
     for (int m = 1; m < 64; m *= 2) {
       const float sg = (lane & m) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int s = 0; s < KB; ++s)
+      for (int s = 0; s < KB; ++s) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float p = __shfl_xor(y[s][j], m);
+          const float p = lane_xor(y[s][j], m, lane);
           y[s][j] = __builtin_fmaf(sg, y[s][j], p);
         }
+      }
     }
 #pragma unroll
     for (int s = 0; s < KB; ++s)
@@ -179,14 +208,15 @@ __global__ __launch_bounds__(64 * RQ_WAVES) void k_rotate(RotArgs a) {
 
     // cross-block mix: z_r = sum_s Q[r][s] y_s, left to right, products rounded first;
     // position by position, in place (y[.][j] is read completely before it is replaced)
+    const float* const Qm = a.Q;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float t[KB];
 #pragma unroll
       for (int r = 0; r < KB; ++r) {
-        t[r] = a.Q[r * KB] * y[0][j];
+        t[r] = Qm[r * KB] * y[0][j];
 #pragma unroll
-        for (int s = 1; s < KB; ++s) t[r] = t[r] + a.Q[r * KB + s] * y[s][j];
+        for (int s = 1; s < KB; ++s) t[r] = t[r] + Qm[r * KB + s] * y[s][j];
       }
 #pragma unroll
       for (int r = 0; r < KB; ++r) y[r][j] = t[r];
