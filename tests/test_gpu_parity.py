@@ -484,6 +484,8 @@ def test_linear_skinny_fused(nv, M, N, seg_end, K, xdt, gate_heads, y_dtype, mod
     (6, 200, [200], 1536, "bf16", 0, "bf16"),          # K % 1024 != 0 with more than four tokens
     (4, 130, [64, 130], 8192, "bf16", 0, "bf16"),      # sixteen K slices (the most), ragged N, two segments
     (2, 64, [64], 1024, "f32", 0, "f32"),              # two K slices (the fewest), fp32 in and out
+    (4, 1, [1], 2048, "bf16", 0, "bf16"),              # one output row: every other weight row clamped
+    (3, 17, [5, 17], 1536, "bf16", 0, "f32"),          # 17 rows, two segments, a partial row group
 ])
 @pytest.mark.parametrize("mode", ["static", "dynamic"])
 @pytest.mark.parametrize("codes_out", [True, False])
