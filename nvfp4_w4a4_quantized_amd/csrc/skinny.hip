@@ -9,11 +9,16 @@
 //
 // Workgroup = 512 threads (8 waves, two per SIMD) = 128 tokens; wave w owns tokens
 // 16w .. 16w+15.  Lane (q = lane >> 4, rr = lane & 15) owns token rr and, in every
-// 128-element unit of K, the 32 elements 32q .. 32q+31: two whole 16-element blocks,
-// so the activation quantizer runs in the lane with no cross-lane step (the same
-// exact arithmetic as the stand-alone quantizer).  The lane's 32 elements feed four
-// MFMA 16x16x32 f16 steps, step t taking elements 8t .. 8t+7 of them; the weight
-// operand uses the same permutation of k, so the sum over k is unchanged.
+// 128-element unit of K, the four octets 32t + 8q .. 32t + 8q + 7 (t = 0..3): load
+// instruction t then reads 64 contiguous bytes of each of the wave's 16 token rows (a
+// lane holding 32 contiguous elements would spread every instruction over twice as many
+// cache lines: 15% slower on the GDN gates shape).  Octet t of lanes q and q ^ 1 (16
+// lanes apart) is one 16-element block: its amax takes one v_permlane16_swap; of the
+// pair's four scale bytes (the stand-alone quantizer's arithmetic) the lane with q even
+// derives those of octets 0 and 1, its partner those of 2 and 3, and two more swaps give
+// both lanes all four (sharing the work: 137 vs 143 us on the GDN gates shape).
+// Octet t is MFMA 16x16x32 f16 step t (K positions 32t + 8q ..); the weight operand is
+// read at the same positions, so the sum over k is unchanged.
 //
 // The weight (N x K packed, a few hundred KiB: L2-resident) is decoded exactly to
 // f16 (e2m1 x E4M3 scale) 256 K-elements at a time into a double-buffered LDS tile
@@ -35,16 +40,21 @@ template <InType T> struct XUnit;                   // 32 elements of one token
 template <> struct XUnit<InType::BF16> { u32x4 q[4]; };
 template <> struct XUnit<InType::F32> { f32x4 q[8]; };
 
+// The lane's four octets of a unit: elem_off = the unit's first element + 8q; octet t
+// is 32t elements further.
 template <InType T>
 __device__ __forceinline__ void xunit_load(const void* base, int64_t elem_off, XUnit<T>& r) {
   if constexpr (T == InType::BF16) {
     const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem_off);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.q[i] = __builtin_nontemporal_load(p + i);
+    for (int i = 0; i < 4; ++i) r.q[i] = __builtin_nontemporal_load(p + 4 * i);
   } else {
     const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + elem_off);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r.q[i] = __builtin_nontemporal_load(p + i);
+    for (int i = 0; i < 4; ++i) {
+      r.q[2 * i] = __builtin_nontemporal_load(p + 8 * i);
+      r.q[2 * i + 1] = __builtin_nontemporal_load(p + 8 * i + 1);
+    }
   }
 }
 
@@ -158,7 +168,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_linear_skinny(GemvArgs p) {
   if (blockIdx.x == 0 && tid == 0 && p.gscale_out != nullptr) *p.gscale_out = g;
 
   const int64_t nu = K / 128;                                        // 128-element units
-  const int64_t xoff = trow * p.ldx + 32 * q;
+  const int64_t xoff = trow * p.ldx + 8 * q;
   XUnit<T> xr[R];
 #pragma unroll
   for (int i = 0; i < R - 1; ++i) xunit_load<T>(p.x, xoff + 128 * min<int64_t>(i, nu - 1), xr[i]);
@@ -189,8 +199,8 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_linear_skinny(GemvArgs p) {
     }
   }
 
-  // B operand: weight row 16 j + rr, chunk column 128 (u % 2) + 32 q + 8 t
-  const uint32_t bbase = (uint32_t)(rr * SK_ROWB + 64 * q);
+  // B operand: weight row 16 j + rr, chunk column 128 (u % 2) + 32 t + 8 q
+  const uint32_t bbase = (uint32_t)(rr * SK_ROWB + 16 * q);
 
   // two chunks (four 128-element units) per iteration, so that every ring and stage
   // index below is a compile-time constant (u0 % 4 == 0; nu is even)
@@ -212,34 +222,55 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_linear_skinny(GemvArgs p) {
       // keep R - 1 units of x in flight (past the end: re-read the last unit)
       xunit_load<T>(p.x, xoff + 128 * min<int64_t>(u + R - 1, nu - 1), xr[(r + R - 1) % R]);
 
-      // quantize the lane's two blocks (elements 32q .. 32q+31 of unit u)
+      // quantize the lane's four octets (block 2t + (q >> 1) of unit u, half q & 1)
       float v[32];
       xunit_unpack<T>(xr[r % R], v);
-      uint32_t sb[2], w[4];
+      uint32_t sb[4], w[4];
+      float am[4];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        float am = __builtin_fabsf(v[16 * b]);
+      for (int t = 0; t < 4; ++t) {
+        am[t] = __builtin_fabsf(v[8 * t]);
 #pragma unroll
-        for (int e = 1; e < 16; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(v[16 * b + e]));
-        sb[b] = block_scale_byte(am, sc);
-        quant16(v + 16 * b, sb[b], g, w + 2 * b);
+        for (int e = 1; e < 8; ++e) am[t] = __builtin_fmaxf(am[t], __builtin_fabsf(v[8 * t + e]));
+        // the other half of the block is in lane ^ 16: the swap of am with itself leaves
+        // both halves' maxima in the two results of either lane
+        const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(am[t]), __float_as_uint(am[t]), false, false);
+        am[t] = __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
       }
+      // the pair shares its four blocks' scales: the lane with q even derives those of
+      // octets 0 and 1, its partner those of octets 2 and 3, and one swap per pair of
+      // scale bytes hands every lane all four (result 0 = the even lane's, 1 = the odd's)
+      {
+        const bool odd = (q & 1) != 0;
+        const uint32_t s0 = block_scale_byte(odd ? am[2] : am[0], sc);
+        const uint32_t s1 = block_scale_byte(odd ? am[3] : am[1], sc);
+        const auto p0 = __builtin_amdgcn_permlane16_swap(s0, s0, false, false);
+        const auto p1 = __builtin_amdgcn_permlane16_swap(s1, s1, false, false);
+        sb[0] = p0[0];
+        sb[2] = p0[1];
+        sb[1] = p1[0];
+        sb[3] = p1[1];
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) w[t] = quant8(v + 8 * t, sb[t], g);
       if constexpr (CODES) {
         // lanes past M quantized row M - 1 (trow) and store the same bytes there
-        *reinterpret_cast<u32x4*>(p.a_codes_out + trow * (K >> 1) + u * 64 + 16 * q) = u32x4{w[0], w[1], w[2], w[3]};
-        *reinterpret_cast<uint16_t*>(p.a_scales_out + trow * (K >> 4) + u * 8 + 2 * q) =
-            (uint16_t)(sb[0] | (sb[1] << 8));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          *reinterpret_cast<uint32_t*>(p.a_codes_out + trow * (K >> 1) + u * 64 + 16 * t + 4 * q) = w[t];
+          if ((q & 1) == 0) p.a_scales_out[trow * (K >> 4) + u * 8 + 2 * t + (q >> 1)] = (uint8_t)sb[t];
+        }
       }
-      // MFMA 16x16x32 steps: A = the lane's elements 8t .. 8t+7, B = weight rows
-      // 16 j + rr at the same K positions
+      // MFMA 16x16x32 steps: A = the lane's octet t, B = weight rows 16 j + rr at the
+      // same K positions
       const uint8_t* bl = sk_lds + cp * WBUF + bbase + 256 * (r & 1);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         // all of this step's weight reads first, the decode of A under them
         f16x8 B[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) B[j] = *reinterpret_cast<const f16x8*>(bl + j * 16 * SK_ROWB + 16 * t);
-        const f16x8 A = decode8_f16(w[t], scale_f16x2(sb[t >> 1]));
+        for (int j = 0; j < NT; ++j) B[j] = *reinterpret_cast<const f16x8*>(bl + j * 16 * SK_ROWB + 64 * t);
+        const f16x8 A = decode8_f16(w[t], scale_f16x2(sb[t]));
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[j], acc[j], 0, 0, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, NT, 0);     // the NT LDS reads
