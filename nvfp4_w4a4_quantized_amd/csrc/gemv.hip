@@ -845,9 +845,7 @@ __global__ __launch_bounds__(64 * G4_MAXW) void k_gemv_k4(GemvArgs p) {
   uint32_t sb[2], qw[4];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    float am = __builtin_fabsf(v[16 * blk]);
-#pragma unroll
-    for (int e = 1; e < 16; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(v[16 * blk + e]));
+    const float am = amax_abs<16>(v + 16 * blk);
     sb[blk] = block_scale_byte(am, sc);
     quant16(v + 16 * blk, sb[blk], g, qw + 2 * blk);
   }

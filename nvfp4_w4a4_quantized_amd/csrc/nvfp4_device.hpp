@@ -167,6 +167,22 @@ __device__ __forceinline__ BlockConsts block_consts(uint32_t sb, float g) {
   return b;
 }
 
+// Largest magnitude of N finite values (N >= 3) by v_max3_f32 with |.| source
+// modifiers: (N - 1) / 2 instructions.  Written out because fmaxf on values the
+// compiler cannot prove canonical (activations unpacked with integer operations) gets
+// an extra canonicalizing max per element.
+template <int N>
+__device__ __forceinline__ float amax_abs(const float* v) {
+  static_assert(N >= 3, "at least three values");
+  float m;
+  asm volatile("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m) : "v"(v[0]), "v"(v[1]), "v"(v[2]));
+#pragma unroll
+  for (int i = 3; i + 1 < N; i += 2)
+    asm volatile("v_max3_f32 %0, %0, |%1|, |%2|" : "+v"(m) : "v"(v[i]), "v"(v[i + 1]));
+  if constexpr (N % 2 == 0) asm volatile("v_max_f32 %0, %0, |%1|" : "+v"(m) : "v"(v[N - 1]));
+  return m;
+}
+
 // 8 values -> 8 E2M1 codes by the hardware RNE conversion (element 0 in the low
 // nibble; saturation at 6, the sign of each value kept)
 __device__ __forceinline__ uint32_t cvt8_fp4(const float* y) {

@@ -106,9 +106,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(const void* __restrict_
     for (int u = 0; u < QU; ++u) {
       float v[16];
       unpack_blk16<T>(raw[u], v);
-      float a = __builtin_fabsf(v[0]);
-#pragma unroll
-      for (int i = 1; i < 16; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+      const float a = amax_abs<16>(v);
       const ScaleConsts sc = sc_lds[seg.n > 1 ? seg_of(seg, row[u] < rows ? row[u] : 0) : 0];
       const uint32_t sb = block_scale_byte(a, sc);
       uint32_t w[2];

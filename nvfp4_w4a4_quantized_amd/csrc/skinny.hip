@@ -229,13 +229,11 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_linear_skinny(GemvArgs p) {
       float am[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        am[t] = __builtin_fabsf(v[8 * t]);
-#pragma unroll
-        for (int e = 1; e < 8; ++e) am[t] = __builtin_fmaxf(am[t], __builtin_fabsf(v[8 * t + e]));
+        am[t] = amax_abs<8>(v + 8 * t);
         // the other half of the block is in lane ^ 16: the swap of am with itself leaves
         // both halves' maxima in the two results of either lane
         const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(am[t]), __float_as_uint(am[t]), false, false);
-        am[t] = __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+        asm volatile("v_max_f32 %0, %1, %2" : "=v"(am[t]) : "v"(pr[0]), "v"(pr[1]));
       }
       // the pair shares its four blocks' scales: the lane with q even derives those of
       // octets 0 and 1, its partner those of octets 2 and 3, and one swap per pair of
