@@ -251,12 +251,15 @@ __device__ __forceinline__ void quant_block(const float v[NV], const BlockConsts
     for (int i = 0; i < NV; ++i) {
       const int d = i / 8, sh = 4 * (i % 8);
       if (all & (1u << (sh + d))) {                            // wave-uniform
-        const uint32_t dn = (w[d] >> sh) & 7u, up = (wh[d] >> sh) & 7u;
+        const uint32_t dn = (w[d] >> sh) & 7u;
         // midpoint between codes dn and dn + 1, times 4: 1 3 5 7 10 14 20 (dn = 0 .. 6)
         const uint32_t m4 = __builtin_amdgcn_perm(0x00140E0Au, 0x07050301u, dn) & 0xFFu;
         const float r = __builtin_fmaf(-((float)m4 * b.s4), g, __builtin_fabsf(v[i]));
         const uint32_t take_up = ((uint32_t)(r > 0.0f) | ((uint32_t)(r == 0.0f) & dn)) & 1u;
-        w[d] += ((dn != up) && take_up ? (up - dn) : 0u) << sh;
+        // where the bracket codes differ they are dn and dn + 1 with the same sign (lo and
+        // hi are x times positive factors): taking the upper one is swapping in hi's
+        // nibble; where they agree the xor is zero and nothing changes
+        w[d] ^= take_up != 0u ? ((w[d] ^ wh[d]) & (0xFu << sh)) : 0u;
       }
     }
   }
