@@ -560,6 +560,65 @@ def _check_linear(nv, M, N, seg_end, K, xdt, gate_heads, y_dtype, mode, codes_ou
     P.assert_within_tolerance(P.y_to_f64(y), yref, bound, f"{what} M={M} N={N} K={K} {xdt} {mode}")
 
 
+def _near_midpoint_rows(rng, M, K, g, xdt):
+    """M x K activations whose 16-element blocks sit on E2M1 midpoints under chosen block
+    scales.  Element 0 of a block is 6 s g, which fixes the block scale to s; the other
+    15 are midpoints m s g (m in 0.25 .. 5) with random signs.  fp32: each moved 0..3 ulps
+    either way (the bracket's fix-up decides them).  bf16: g is a power of two, so m s g
+    has <= 7 significant bits and is an exact bf16 value: every such element is a tie."""
+    x = np.zeros((M, K), dtype=np.float32)
+    for r in range(M):
+        for b in range(K // 16):
+            s = float(O.e4m3_value(int(rng.integers(0x20, 0x7F))))
+            blk = np.empty(16, dtype=np.float32)
+            blk[0] = np.float32(6 * s * g)
+            mids = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], size=15)
+            v = (mids * s * g).astype(np.float32)
+            if xdt == "f32":
+                v = (v.view(np.int32) + rng.integers(-3, 4, size=15).astype(np.int32)).view(np.float32)
+            blk[1:] = v * rng.choice([-1, 1], size=15).astype(np.float32)
+            x[r, 16 * b:16 * b + 16] = blk
+    return x
+
+
+@pytest.mark.parametrize("M,N,K,xdt", [
+    (70, 96, 512, "f32"),       # fused skinny kernel
+    (70, 96, 512, "bf16"),
+    (4, 64, 1024, "f32"),       # decode GEMV, MFMA 4x4x4
+    (4, 64, 1024, "bf16"),
+    (7, 64, 1024, "bf16"),      # decode GEMV, 5..8 tokens
+])
+def test_linear_fused_near_midpoints(nv, M, N, K, xdt):
+    """Activations on and around E2M1 midpoints through the fused linear kernels, which
+    quantize x in registers: codes and scales bit-exact with the oracle (the near-midpoint
+    fix-up decides every flagged element), outputs within the GEMM tolerance."""
+    rng = np.random.default_rng(M * 101 + K + (7 if xdt == "bf16" else 0))
+    g = 0.0173 if xdt == "f32" else 2.0 ** -6
+    x = _near_midpoint_rows(rng, M, K, g, xdt)
+    if xdt == "bf16":
+        bits = W._to_bf16_bits(x)
+        xv = W.bf16_bits_to_f32(bits)
+        assert np.array_equal(xv, x)                                # every value exact in bf16
+        xt = P.dev_x(xv, bits)
+    else:
+        xv, xt = x, P.dev_x(x)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    seg_end = [N]
+    wc, ws, wg = P.gpu_pack(nv, P.dev_x(w), seg_end, None)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    gin = torch.tensor([g], dtype=torch.float32, device="cuda")
+    gout = torch.empty(1, dtype=torch.float32, device="cuda")
+    ac, as_ = nv.empty_packed(M, K, "cuda")
+    nv.nvfp4_w4a4_linear(xt, gin, gout, wc, ws, seg_end, wg, y, a_codes_out=ac, a_scales_out=as_)
+    torch.cuda.synchronize()
+    oc, os_, og = O.quantize_activation(P.x64_of(xv), np.float32(g))
+    owc, ows, owg = O.pack_weight(w.astype(np.float64), seg_end)
+    P.assert_bytes_equal(as_.cpu().numpy(), os_, "activation scales")
+    P.assert_bytes_equal(ac.cpu().numpy(), oc, "activation codes")
+    yref, _, bound = P.oracle_reference(oc, os_, og, owc, ows, seg_end, owg, "bf16")
+    P.assert_within_tolerance(P.y_to_f64(y), yref, bound, f"near-midpoint M={M} N={N} K={K} {xdt}")
+
+
 def test_linear_skinny_equals_two_stage(nv):
     """Fused skinny path and the two-stage path (quantize, then GEMM) agree to the
     GEMM tolerance on the same inputs; their activation codes are identical."""
