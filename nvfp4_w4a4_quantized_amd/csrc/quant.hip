@@ -23,8 +23,7 @@ __device__ __forceinline__ int seg_of(const SegTable& seg, int64_t row) {
 // fp32 loads), so the block amax needs no cross-lane step and the block scale is
 // computed once per block.  One wave = a "segment" of 64 consecutive blocks (1024
 // elements) of one row; QU segments per iteration with all their loads issued
-// before any is used (ordinary loads: the non-temporal form was 2-14% slower at
-// 8192 x 5120, the larger gap when x is still in the infinity cache).  Segment -> (row, block)
+// (non-temporal: x is read once) before any is used.  Segment -> (row, block)
 // bookkeeping is wave-uniform and runs on the scalar unit.  The per-segment scale
 // constants (global scale and fp32(1/(6g))) are computed once per workgroup into LDS.
 constexpr int QU = 4;
@@ -37,14 +36,14 @@ template <InType T>
 __device__ __forceinline__ void load_blk16(const void* base, int64_t elem_off, Blk16<T>& r) {
   if constexpr (T == InType::BF16) {
     const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem_off);
-    r.a = p[0];
-    r.b = p[1];
+    r.a = __builtin_nontemporal_load(p);
+    r.b = __builtin_nontemporal_load(p + 1);
   } else {
     const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + elem_off);
-    r.a = p[0];
-    r.b = p[1];
-    r.c = p[2];
-    r.d = p[3];
+    r.a = __builtin_nontemporal_load(p);
+    r.b = __builtin_nontemporal_load(p + 1);
+    r.c = __builtin_nontemporal_load(p + 2);
+    r.d = __builtin_nontemporal_load(p + 3);
   }
 }
 
