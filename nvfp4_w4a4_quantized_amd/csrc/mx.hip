@@ -265,7 +265,9 @@ __global__ __launch_bounds__(256, 1) void k_mx_gemm(MxArgs a) {
   // drops their stores; columns past N are masked per lane.  The host guarantees that
   // no offset wraps 32 bits ((M + 264) * ldy * size < 2^32), an even ldy, and for bf16
   // output an even N (pairs of adjacent columns are stored as one 32-bit word, built
-  // across neighbouring lanes with DPP, as in the NVFP4 prefill kernel).
+  // across neighbouring lanes with DPP, as in the NVFP4 prefill kernel).  The stores
+  // are non-temporal (cache policy nt), which keeps the output out of the caches the
+  // operand tiles are re-read through: 0.517 -> 0.475 ms at 8192 x 16384 x 5120.
   constexpr int ESZ = BF16OUT ? 2 : 4;
   const int64_t extent = ((a.M - 1) * a.ldy + a.N) * ESZ;
   const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, (int)(uint32_t)extent, 0x00020000);
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(256, 1) void k_mx_gemm(MxArgs a) {
           const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp((int)pk, (int)pk, 0xB1, 0xF, 0xF, false);
           const uint32_t word = __builtin_amdgcn_perm(nb, pk, sel);
           const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (p >> 1) + 2 * (p & 1)) * ldyb + (uint32_t)(j * 64);
-          if (col_ok) __builtin_amdgcn_raw_buffer_store_b32(word, yr, voff, soff, 0);
+          if (col_ok) __builtin_amdgcn_raw_buffer_store_b32(word, yr, voff, soff, 2);
         }
     }
   } else {
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(256, 1) void k_mx_gemm(MxArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t soff = tile_off + (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldyb + (uint32_t)(j * 128);
-          if (col_ok) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), yr, voff, soff, 0);
+          if (col_ok) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), yr, voff, soff, 2);
         }
     }
   }
