@@ -74,7 +74,9 @@ __device__ __forceinline__ uint32_t requant_block(u32x2& w, uint32_t sb, float g
 }
 
 // One lane = BPL consecutive blocks of one row (kb % BPL == 0): BPL * 8 bytes of
-// codes and BPL scale bytes, read and written with vector accesses.  Group indices
+// codes and BPL scale bytes, read and written with vector accesses; the four-block
+// form writes non-temporally (the re-encoded weight is not read back soon: 23.2 ->
+// 20.2 us on the 16384 x 5120 weight).  Group indices
 // fit 32 bits (checked on the host).
 template <int BPL>
 __global__ __launch_bounds__(256) void k_requantize(const uint8_t* codes, const uint8_t* scales, uint32_t groups,
@@ -101,9 +103,9 @@ __global__ __launch_bounds__(256) void k_requantize(const uint8_t* codes, const 
       uint32_t ns = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) ns |= requant_block(w[j], (s4 >> (8 * j)) & 0xFFu, gs, gsh) << (8 * j);
-      *reinterpret_cast<u32x4*>(codes_out + 8 * b0) = u32x4{w[0][0], w[0][1], w[1][0], w[1][1]};
-      *reinterpret_cast<u32x4*>(codes_out + 8 * b0 + 16) = u32x4{w[2][0], w[2][1], w[3][0], w[3][1]};
-      *reinterpret_cast<uint32_t*>(scales_out + b0) = ns;
+      __builtin_nontemporal_store(u32x4{w[0][0], w[0][1], w[1][0], w[1][1]}, reinterpret_cast<u32x4*>(codes_out + 8 * b0));
+      __builtin_nontemporal_store(u32x4{w[2][0], w[2][1], w[3][0], w[3][1]}, reinterpret_cast<u32x4*>(codes_out + 8 * b0 + 16));
+      __builtin_nontemporal_store(ns, reinterpret_cast<uint32_t*>(scales_out + b0));
     } else {
       u32x2 w = *reinterpret_cast<const u32x2*>(codes + 8 * b0);
       const uint32_t nb = requant_block(w, scales[b0], gs, gsh);
